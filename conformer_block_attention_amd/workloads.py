@@ -1,0 +1,182 @@
+"""Seeded synthetic workloads for the block-local MHSA sub-layer.
+
+This module only draws random numbers and lays them out; it holds none of the
+sub-layer's arithmetic. Both the HIP path and the CPU oracle are fed from here.
+
+Where the shapes come from (IBM Granite-Speech-4.1-2B-NAR pages):
+  * model card, "Model Architecture" (1) CTC Speech Encoder: 16-layer conformer,
+    80 log-mel bins with 2-frame stacking, block attention over 4-second blocks.
+  * ONNX-export README, "Parity": an 8.43 s clip gives 844 mel frames, i.e. a
+    100 Hz mel rate; 2-frame stacking halves it to 50 Hz, so one clip of that
+    length is 422 encoder frames and a 4-second block is 200 frames.
+  * portable-INT4 README, "What Changed" item 4: a fixed [1, 800, 160] encoder
+    bucket, i.e. 800 frames (16 s) of 160 = 80 x 2 stacked features.
+  * ONNX-export README, "Multi-clip transcript parity": clips of 39 to 94 s,
+    i.e. 1950 to 4700 frames.
+  * model card, "Additional results": batched inference at batch size 128;
+    portable-INT4 README, "Validation": mean utterance 8.47 s, about 425 frames.
+
+The pages measure on LibriSpeech clips and the Open ASR leaderboard sets; none of
+that audio is used. These synthetic inputs stand in for it, with the same frame
+counts and batch sizes.
+
+Random-number recipe (one documented generator, shared by both sides):
+  numpy PCG64 seeded by SeedSequence(seed, spawn_key=(stream,)), with stream
+  0 = sequence lengths, 1 = activations x, 2 + 2*l = Wqkv of layer l,
+  3 + 2*l = Wo of layer l.  x ~ N(0, 1); weights ~ N(0, 1/d_model), reading the
+  second parameter as a variance (std = d_model**-0.5, exactly 1/32 at 1024).
+  Values are drawn in float32; bf16 workloads round them to bfloat16 with
+  round-to-nearest-even (torch's float->bfloat16 cast) before either side sees
+  them, so both sides read identical numbers.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+# Frame rate after 2-frame stacking and the block length it implies.
+ENCODER_FRAME_HZ = 50
+BLOCK_SECONDS = 4
+BLOCK_FRAMES = ENCODER_FRAME_HZ * BLOCK_SECONDS  # 200
+
+STREAM_LENGTHS = 0
+STREAM_X = 1
+
+
+def _rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream,))))
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: sizes, dtype and the recipe for its lengths."""
+
+    name: str
+    dtype: str                # "fp32" or "bf16"
+    length_kind: str          # "fixed" | "uniform" | "lognormal"
+    num_seqs: int
+    d_model: int = 1024
+    heads: int = 8
+    block_frames: int = BLOCK_FRAMES
+    layers: int = 1
+    seed: int = 0
+    fixed_length: int = 0     # for "fixed"
+    lo: int = 0               # "uniform": closed range [lo, hi]; "lognormal": clip range
+    hi: int = 0
+    mean: float = 0.0         # "lognormal": arithmetic mean of the unclipped draw
+    sigma: float = 0.0        # "lognormal": log-space standard deviation
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    def lengths(self) -> np.ndarray:
+        return draw_lengths(self)
+
+
+def draw_lengths(w: Workload) -> np.ndarray:
+    """Sequence lengths in generation (packing) order, int64."""
+    if w.length_kind == "fixed":
+        return np.full(w.num_seqs, w.fixed_length, dtype=np.int64)
+    g = _rng(w.seed, STREAM_LENGTHS)
+    if w.length_kind == "uniform":
+        # integers uniform on the closed range [lo, hi]
+        return g.integers(w.lo, w.hi, size=w.num_seqs, endpoint=True).astype(np.int64)
+    if w.length_kind == "lognormal":
+        # arithmetic mean `mean` => mu = ln(mean) - sigma^2 / 2; round half-even; clip
+        mu = math.log(w.mean) - 0.5 * w.sigma * w.sigma
+        raw = g.lognormal(mean=mu, sigma=w.sigma, size=w.num_seqs)
+        return np.clip(np.rint(raw), w.lo, w.hi).astype(np.int64)
+    raise ValueError(f"unknown length kind {w.length_kind!r}")
+
+
+# The five workloads, in the order the headline configurations are listed.
+WORKLOADS = {
+    "fp32_t422": Workload("fp32_t422", "fp32", "fixed", 1, fixed_length=422),
+    "bf16_t800": Workload("bf16_t800", "bf16", "fixed", 1, fixed_length=800),
+    "bf16_b32_long": Workload("bf16_b32_long", "bf16", "uniform", 32, lo=1950, hi=4700),
+    "bf16_b128_lognormal": Workload("bf16_b128_lognormal", "bf16", "lognormal", 128,
+                                    lo=100, hi=1750, mean=425.0, sigma=0.35),
+    "bf16_b128_chain16": Workload("bf16_b128_chain16", "bf16", "lognormal", 128,
+                                  lo=100, hi=1750, mean=425.0, sigma=0.35, layers=16),
+}
+WORKLOAD_ORDER = list(WORKLOADS)
+HEADLINE = "bf16_b128_lognormal"
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """Exclusive prefix sum of lengths, int32 [S+1] (cu[0] = 0, cu[S] = N)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=cu[1:])
+    if cu[-1] > np.iinfo(np.int32).max:
+        raise ValueError("total frames exceed int32")
+    return cu.astype(np.int32)
+
+
+def normal(seed: int, stream: int, shape, std: float = 1.0) -> torch.Tensor:
+    """float32 N(0, std^2) draw from sub-stream `stream` (CPU tensor)."""
+    g = _rng(seed, stream)
+    a = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return torch.from_numpy(a)
+
+
+def make_x(n_frames: int, d_model: int, dtype: torch.dtype, seed: int = 0) -> torch.Tensor:
+    return normal(seed, STREAM_X, (n_frames, d_model)).to(dtype)
+
+
+def make_weights(d_model: int, dtype: torch.dtype, seed: int = 0, layer: int = 0):
+    """(Wqkv [3d, d], Wo [d, d]) in nn.Linear [out, in] layout."""
+    std = 1.0 / math.sqrt(d_model)
+    wqkv = normal(seed, 2 + 2 * layer, (3 * d_model, d_model), std).to(dtype)
+    wo = normal(seed, 3 + 2 * layer, (d_model, d_model), std).to(dtype)
+    return wqkv, wo
+
+
+@dataclasses.dataclass
+class Case:
+    """Materialised inputs of one workload (CPU tensors)."""
+
+    name: str
+    lengths: np.ndarray
+    cu: np.ndarray
+    x: torch.Tensor
+    weights: list            # [(Wqkv, Wo)] per layer
+    block_frames: int
+    heads: int
+    dtype: torch.dtype
+
+    @property
+    def n_frames(self) -> int:
+        return int(self.cu[-1])
+
+    @property
+    def d_model(self) -> int:
+        return int(self.x.shape[1])
+
+
+def build_case(w: Workload, layers: Optional[int] = None) -> Case:
+    lengths = w.lengths()
+    cu = cu_seqlens(lengths)
+    n = int(cu[-1])
+    x = make_x(n, w.d_model, w.torch_dtype, w.seed)
+    nl = w.layers if layers is None else layers
+    weights = [make_weights(w.d_model, w.torch_dtype, w.seed, l) for l in range(nl)]
+    return Case(w.name, lengths, cu, x, weights, w.block_frames, w.heads, w.torch_dtype)
+
+
+def custom_case(lengths, d_model: int, heads: int, block_frames: int, dtype: torch.dtype,
+                seed: int = 0, layers: int = 1, name: str = "custom") -> Case:
+    """Inputs for arbitrary small shapes (tests): same recipe, given lengths."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = cu_seqlens(lengths)
+    n = int(cu[-1])
+    x = make_x(n, d_model, dtype, seed)
+    weights = [make_weights(d_model, dtype, seed, l) for l in range(layers)]
+    return Case(name, lengths, cu, x, weights, block_frames, heads, dtype)

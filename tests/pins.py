@@ -1,0 +1,284 @@
+"""Checks that pin the CPU oracle to facts other than itself.
+
+Each `pin_*` takes an oracle handle and raises AssertionError on a mismatch.
+They are collected by test_oracle_pins.py (against the real oracle) and by
+test_oracle_mutants.py (against copies of the oracle with planted mistakes,
+each of which at least one pin must reject).
+
+What the sub-layer is (IBM model card, "Model Architecture" (1): block
+attention over 4-second blocks in every conformer layer; usage section:
+sequence packing with non-causal attention): per block of at most B rows,
+restarting at every sequence, softmax(Q K^T / sqrt(dh)) V per head, then the
+output projection plus the residual.
+
+Independent references used here:
+  * closed form for B = 1 (every block is one row, softmax weight 1):
+    out = x + (x Wv^T) Wo^T
+  * torch's scaled_dot_product_attention (CPU, float64) when one block covers
+    a whole sequence
+  * a brute-force masked full-attention computation in numpy
+  * exact invariances (packing, block/sequence split, locality, zero weights,
+    power-of-two rescaling, constant rows, uniform attention)
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def rand_problem(lengths, d=32, heads=2, seed=0, wscale=None):
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, np.int64)
+    n = int(lengths.sum())
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    s = (1.0 / np.sqrt(d)) if wscale is None else wscale
+    x = rng.standard_normal((n, d))
+    wqkv = rng.standard_normal((3 * d, d)) * s
+    wo = rng.standard_normal((d, d)) * s
+    return x, cu, wqkv, wo
+
+
+def brute_force(x, cu, wqkv, wo, block, heads):
+    """Full N x N attention with a mask allowing only same-sequence, same-block pairs."""
+    n, d = x.shape
+    dh = d // heads
+    qkv = x @ wqkv.T
+    seq = np.zeros(n, np.int64)
+    pos = np.zeros(n, np.int64)
+    for s in range(len(cu) - 1):
+        seq[cu[s]:cu[s + 1]] = s
+        pos[cu[s]:cu[s + 1]] = np.arange(cu[s + 1] - cu[s])
+    blk = pos // block
+    allowed = (seq[:, None] == seq[None, :]) & (blk[:, None] == blk[None, :])
+    o = np.zeros((n, d))
+    for h in range(heads):
+        q = qkv[:, h * dh:(h + 1) * dh]
+        k = qkv[:, d + h * dh:d + (h + 1) * dh]
+        v = qkv[:, 2 * d + h * dh:2 * d + (h + 1) * dh]
+        z = (q @ k.T) / np.sqrt(dh)
+        z = np.where(allowed, z, -np.inf)
+        z = z - z.max(axis=1, keepdims=True)
+        p = np.exp(z)
+        p /= p.sum(axis=1, keepdims=True)
+        o[:, h * dh:(h + 1) * dh] = p @ v
+    return x + o @ wo.T
+
+
+def rel_err(a, b):
+    scale = np.sqrt(np.mean(np.square(b))) if b.size else 1.0
+    return float(np.max(np.abs(a - b)) / max(scale, 1e-300)) if b.size else 0.0
+
+
+# ---------------------------------------------------------------------------
+# pins
+
+def pin_block1_closed_form(orc):
+    """B = 1: each row attends only to itself, so out = x + (x Wv^T) Wo^T."""
+    x, cu, wqkv, wo = rand_problem([5, 3, 7], d=32, heads=4, seed=1)
+    d = x.shape[1]
+    ref = x + (x @ wqkv[2 * d:].T) @ wo.T
+    got = orc.block_mhsa(x, cu, wqkv, wo, 1, 4)
+    assert rel_err(got, ref) < 1e-13, rel_err(got, ref)
+
+
+def pin_full_attention_sdpa(orc):
+    """B >= every length: per-sequence full bidirectional attention (library routine)."""
+    lengths = [9, 1, 17, 4]
+    heads, d = 4, 32
+    dh = d // heads
+    x, cu, wqkv, wo = rand_problem(lengths, d=d, heads=heads, seed=2, wscale=0.4)
+    got = orc.block_mhsa(x, cu, wqkv, wo, 1000, heads)
+    xt = torch.from_numpy(x)
+    W = torch.from_numpy(wqkv)
+    ref = np.zeros_like(x)
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        xs = xt[a:b]
+        q = (xs @ W[:d].T).reshape(b - a, heads, dh).transpose(0, 1)
+        k = (xs @ W[d:2 * d].T).reshape(b - a, heads, dh).transpose(0, 1)
+        v = (xs @ W[2 * d:].T).reshape(b - a, heads, dh).transpose(0, 1)
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=False)
+        o = o.transpose(0, 1).reshape(b - a, d).numpy()
+        ref[a:b] = x[a:b] + o @ wo.T
+    assert rel_err(got, ref) < 1e-12, rel_err(got, ref)
+
+
+def pin_brute_force_mask(orc):
+    """Blocks restart at each sequence; tails are partial (brute-force masked attention)."""
+    cases = [([7, 3, 12, 1, 9], 4, 4), ([20], 6, 2), ([5, 5, 5], 2, 1), ([13, 2], 16, 4),
+             ([11, 4, 9], 5, 2)]
+    for i, (lengths, block, heads) in enumerate(cases):
+        x, cu, wqkv, wo = rand_problem(lengths, d=32, heads=heads, seed=10 + i, wscale=0.35)
+        got = orc.block_mhsa(x, cu, wqkv, wo, block, heads)
+        ref = brute_force(x, cu, wqkv, wo, block, heads)
+        assert rel_err(got, ref) < 1e-12, (lengths, block, heads, rel_err(got, ref))
+
+
+def pin_packing_invariance(orc):
+    """Packing sequences equals running them one at a time (bitwise)."""
+    lengths = [6, 11, 3, 8]
+    x, cu, wqkv, wo = rand_problem(lengths, d=32, heads=2, seed=3)
+    packed = orc.block_mhsa(x, cu, wqkv, wo, 4, 2)
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        one = orc.block_mhsa(x[a:b], np.array([0, b - a], np.int32), wqkv, wo, 4, 2)
+        assert np.array_equal(one, packed[a:b]), s
+
+
+def pin_block_split(orc):
+    """Cutting every sequence at its block boundaries and using B = inf gives the same bits."""
+    lengths = [10, 7]
+    B = 4
+    x, cu, wqkv, wo = rand_problem(lengths, d=32, heads=2, seed=4)
+    ref = orc.block_mhsa(x, cu, wqkv, wo, B, 2)
+    pieces = []
+    for ln in lengths:
+        pieces += [min(B, ln - j) for j in range(0, ln, B)]
+    cu2 = np.zeros(len(pieces) + 1, np.int32)
+    cu2[1:] = np.cumsum(pieces)
+    got = orc.block_mhsa(x, cu2, wqkv, wo, 10 ** 6, 2)
+    assert np.array_equal(got, ref)
+
+
+def pin_locality(orc):
+    """Changing the rows of one block changes only that block's outputs."""
+    x, cu, wqkv, wo = rand_problem([9, 6], d=32, heads=2, seed=5)
+    B = 4  # blocks: [0,4) [4,8) [8,9) [9,13) [13,15)
+    ref = orc.block_mhsa(x, cu, wqkv, wo, B, 2)
+    x2 = x.copy()
+    x2[4:8] += 0.5
+    got = orc.block_mhsa(x2, cu, wqkv, wo, B, 2)
+    keep = np.ones(len(x), bool)
+    keep[4:8] = False
+    assert np.array_equal(got[keep], ref[keep])
+    assert np.all(np.abs(got[4:8] - ref[4:8]).max(axis=1) > 0)
+
+
+def pin_zero_weights(orc):
+    """Wo = 0 or Wv = 0 leaves out == x exactly."""
+    x, cu, wqkv, wo = rand_problem([5, 9], d=32, heads=2, seed=6)
+    d = x.shape[1]
+    got = orc.block_mhsa(x, cu, wqkv, np.zeros_like(wo), 3, 2)
+    assert np.array_equal(got, x)
+    w = wqkv.copy()
+    w[2 * d:] = 0
+    got = orc.block_mhsa(x, cu, w, wo, 3, 2)
+    assert np.array_equal(got, x)
+
+
+def pin_power_of_two_qk(orc):
+    """Scaling Wq by 2^k and Wk by 2^-k leaves every logit, hence the output, bit-identical."""
+    x, cu, wqkv, wo = rand_problem([8, 5], d=32, heads=2, seed=7)
+    d = x.shape[1]
+    w = wqkv.copy()
+    w[:d] *= 8.0
+    w[d:2 * d] *= 0.125
+    a = orc.block_mhsa(x, cu, wqkv, wo, 3, 2)
+    b = orc.block_mhsa(x, cu, w, wo, 3, 2)
+    assert np.array_equal(a, b)
+
+
+def pin_permutation_within_block(orc):
+    """Permuting rows inside one block permutes that block's outputs (bidirectional, no position)."""
+    x, cu, wqkv, wo = rand_problem([10], d=32, heads=2, seed=8)
+    ref = orc.block_mhsa(x, cu, wqkv, wo, 5, 2)
+    perm = np.arange(10)
+    perm[5:] = [8, 5, 9, 7, 6]
+    got = orc.block_mhsa(x[perm], cu, wqkv, wo, 5, 2)
+    assert rel_err(got, ref[perm]) < 1e-13
+
+
+def pin_constant_rows(orc):
+    """All rows of a block equal: every weight is 1/L, so out = x + v Wo^T for each row."""
+    x, cu, wqkv, wo = rand_problem([6], d=32, heads=2, seed=9)
+    d = x.shape[1]
+    x[:] = x[0]
+    got = orc.block_mhsa(x, cu, wqkv, wo, 6, 2)
+    ref = x + (x @ wqkv[2 * d:].T) @ wo.T
+    assert rel_err(got, ref) < 1e-13
+
+
+def pin_uniform_attention(orc):
+    """Wq = 0: all logits are 0, so each row gets the mean value row of its own block."""
+    lengths = [9, 4, 7]
+    B = 4
+    x, cu, wqkv, wo = rand_problem(lengths, d=32, heads=2, seed=11)
+    d = x.shape[1]
+    w = wqkv.copy()
+    w[:d] = 0
+    got = orc.block_mhsa(x, cu, w, wo, B, 2)
+    v = x @ wqkv[2 * d:].T
+    mean_v = np.zeros_like(v)
+    for s in range(len(lengths)):
+        for a in range(int(cu[s]), int(cu[s + 1]), B):
+            b = min(a + B, int(cu[s + 1]))
+            mean_v[a:b] = v[a:b].mean(axis=0)
+    ref = x + mean_v @ wo.T
+    assert rel_err(got, ref) < 1e-13
+
+
+def pin_empty_and_degenerate(orc):
+    """Zero-length sequences produce no rows; all-empty packs are a no-op; B > N is full attention."""
+    x, cu, wqkv, wo = rand_problem([0, 5, 0, 0, 3, 0], d=32, heads=2, seed=12)
+    got = orc.block_mhsa(x, cu, wqkv, wo, 2, 2)
+    ref = orc.block_mhsa(x, np.array([0, 5, 8], np.int32), wqkv, wo, 2, 2)
+    assert np.array_equal(got, ref)
+    empty = orc.block_mhsa(np.zeros((0, 32)), np.zeros(3, np.int32), wqkv, wo, 2, 2)
+    assert empty.shape == (0, 32)
+
+
+def pin_golden_block_tables(orc):
+    """Block tables of the 8.43 s clip (422 frames) and the 800-frame bucket (cited fixtures)."""
+    for name in ("block_table_t422.txt", "block_table_bucket800.txt"):
+        rows, frames, block = [], None, None
+        with open(os.path.join(GOLDEN, name)) as f:
+            for line in f:
+                line = line.split("#")[0].strip()
+                if not line:
+                    continue
+                k, v = line.split()
+                if k == "frames":
+                    frames = int(v)
+                elif k == "block_frames":
+                    block = int(v)
+                else:
+                    rows.append((int(k), int(v)))
+        st, ln = orc.block_table(np.array([0, frames], np.int32), block)
+        assert list(zip(st.tolist(), ln.tolist())) == rows, name
+
+
+def pin_row_mask(orc):
+    """Computing selected rows only gives the same bits as the full computation."""
+    x, cu, wqkv, wo = rand_problem([9, 6, 11], d=32, heads=2, seed=13)
+    ref = orc.block_mhsa(x, cu, wqkv, wo, 4, 2)
+    mask = np.zeros(len(x), np.uint8)
+    mask[[0, 5, 10, 17, 25]] = 1
+    got = orc.block_mhsa(x, cu, wqkv, wo, 4, 2, mask=mask)
+    sel = mask.astype(bool)
+    assert np.array_equal(got[sel], ref[sel])
+    assert np.all(np.isnan(got[~sel]))
+
+
+def pin_thread_invariance(orc):
+    x, cu, wqkv, wo = rand_problem([13, 7, 9], d=32, heads=4, seed=14)
+    a = orc.block_mhsa(x, cu, wqkv, wo, 5, 4, nthreads=1)
+    b = orc.block_mhsa(x, cu, wqkv, wo, 5, 4, nthreads=7)
+    assert np.array_equal(a, b)
+
+
+def pin_stages_compose(orc):
+    """The staged entry points compose to the whole sub-layer, bit for bit."""
+    x, cu, wqkv, wo = rand_problem([7, 10], d=32, heads=2, seed=15)
+    qkv = orc.qkv_proj(x, wqkv)
+    o = orc.block_attn(qkv, cu, 2, 3)
+    out = orc.out_proj_residual(o, wo, x)
+    assert np.array_equal(out, orc.block_mhsa(x, cu, wqkv, wo, 3, 2))
+    assert rel_err(qkv, x @ wqkv.T) < 1e-13
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
