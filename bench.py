@@ -1,0 +1,203 @@
+"""Throughput of the block-local MHSA sub-layer on one MI355X.
+
+One step = one call of gs_block_mhsa_fwd (Q|K|V projection, block attention,
+output projection with residual) over the whole packed batch, inputs already
+resident in HBM.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from conformer_block_attention_amd import accounting, gsattn, workloads  # noqa: E402
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+F32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+KERNELS = ("qkv_proj", "block_attn", "out_proj")
+KERNEL_SOURCES = {
+    "qkv_proj": ["gemm_bf16.hip"],
+    "out_proj": ["gemm_bf16.hip"],
+    "block_attn": ["attn_bf16.hip", "attn_units.hpp"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + ["gs_device.hpp"]:
+        with open(os.path.join(ROOT, "conformer_block_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash(kernel):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """The CPU oracle, untuned, on whole sequences of the workload in packing order
+    until about `budget_s` seconds have passed."""
+    import oracle
+
+    orc = oracle.load()
+    nthreads = min(os.cpu_count() or 1, 16)
+    wqkv, wo = case.weights[0]
+    w1, w2 = wqkv.double().numpy(), wo.double().numpy()
+    frames = 0
+    seqs = 0
+    t0 = time.perf_counter()
+    for s in range(len(case.lengths)):
+        a, b = int(case.cu[s]), int(case.cu[s + 1])
+        xs = case.x[a:b].double().numpy()
+        orc.block_mhsa(xs, np.array([0, b - a], np.int32), w1, w2, case.block_frames, case.heads,
+                       nthreads=nthreads)
+        frames += b - a
+        seqs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": frames / el, "unit": "frames/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"first {seqs} of {len(case.lengths)} sequences ({frames} frames), "
+                      f"one layer, fp64, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=workloads.WORKLOAD_ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the sub-layer shards by whole sequences with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w = workloads.WORKLOADS[args.workload]
+    case = workloads.build_case(w, layers=w.layers)
+    dev = torch.device("cuda:0")
+    x = case.x.to(dev)
+    cu = torch.from_numpy(case.cu).to(dev)
+    weights = [(a.to(dev), b.to(dev)) for a, b in case.weights]
+    n, d = x.shape
+    nl = len(weights)
+    ws = gsattn.alloc_workspace(n, d, x.dtype, dev)
+    bufs = [torch.empty_like(x), torch.empty_like(x)]
+    stream = torch.cuda.current_stream()
+
+    def step(events=None, ev_base=0):
+        cur = x
+        for l, (wqkv, wo) in enumerate(weights):
+            o = bufs[l & 1]
+            gsattn.block_mhsa_fwd(cur, cu, wqkv, wo, case.block_frames, case.heads, out=o,
+                                  workspace=ws, stream=stream,
+                                  kernel_events=events.view(ev_base + 4 * l) if events else None)
+            cur = o
+        return cur
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = gsattn.HipEvents(4 * nl * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev, 4 * nl * k)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+
+    per = {k: [] for k in KERNELS}
+    for i in range(nl * args.steps):
+        b = 4 * i
+        per["qkv_proj"].append(ev.elapsed_ms(b, b + 1))
+        per["block_attn"].append(ev.elapsed_ms(b + 1, b + 2))
+        per["out_proj"].append(ev.elapsed_ms(b + 2, b + 3))
+    avg_ms = {k: float(np.mean(v)) for k, v in per.items()}
+
+    ms_step = el / args.steps * 1e3
+    frames_per_s = n * nl / (el / args.steps)  # frame-layers per second
+    fl = accounting.useful_flops(case.lengths, d, case.block_frames)
+    tflops = fl["total"] * nl / (el / args.steps) / 1e12
+    bf16 = x.dtype == torch.bfloat16
+    peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
+    elem = 2 if bf16 else 4
+    by = accounting.algorithmic_bytes(n, d, elem)
+
+    # dominant kernel and its roofline
+    dom = max(avg_ms, key=avg_ms.get)
+    if dom == "block_attn":
+        achieved = by["block_attn"] / (avg_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = fl[dom] / (avg_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof["kernel"] = dom
+    roof["traffic"] = traffic_for(dom) if bf16 else None
+
+    kernels = {}
+    for k in KERNELS:
+        kernels[k] = {"avg_ms": avg_ms[k],
+                      "tflops": fl[k] / (avg_ms[k] * 1e-3) / 1e12,
+                      "alg_GBs": by[k] / (avg_ms[k] * 1e-3) / 1e9}
+
+    rec = {
+        "metric": "encoder frames/sec through block-MHSA (bf16, B=128 packed); % bf16 MFMA peak",
+        "value": frames_per_s,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": int(len(case.lengths)), "frames": int(n),
+                   "blocks": len(accounting.block_table(case.lengths, case.block_frames)),
+                   "block_frames": case.block_frames, "d_model": int(d), "heads": case.heads,
+                   "layers": nl, "seed": w.seed},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / peak,
+        "useful_gflop_per_layer": fl["total"] / 1e9,
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,80 @@
+// attn_units.hpp -- work units of the block-attention kernels.
+//
+// A block is a run of at most B consecutive rows of one sequence; blocks
+// restart at every cu_seqlens boundary and the last block of a sequence holds
+// the remainder.  A work unit is one block, or a group of at most QG query rows
+// of a block when B > QG.  Units are numbered sequence by sequence, block by
+// block, and are located on the device from cu_seqlens alone.
+#pragma once
+
+#include "gs_device.hpp"
+
+namespace gs {
+
+struct AttnUnit {
+  int row0;   // first row of the block
+  int L;      // block length (keys)
+  int q0;     // first query row of the unit (block-relative)
+  int qn;     // number of query rows
+};
+
+// Units of one sequence of `len` rows: full blocks need upb = ceil(B/QG)
+// units each, the last block ceil(tail/QG).
+template <int QG>
+__device__ __forceinline__ int units_of_seq(int len, int B, int upb) {
+  if (len <= 0) return 0;
+  const int nb = (len - 1) / B + 1;
+  const int tail = len - (nb - 1) * B;
+  return (nb - 1) * upb + (tail + QG - 1) / QG;
+}
+
+// Wave-level search for unit u (every lane gets the result).  Sequences are
+// scanned 64 at a time with a wave prefix sum.  False if u is past the end.
+template <int QG>
+__device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnUnit& out) {
+  const int lane = threadIdx.x & 63;
+  const int upb = (B - 1) / QG + 1;
+  int base = 0;
+  for (int c0 = 0; c0 < S; c0 += 64) {
+    const int s = c0 + lane;
+    int len = 0;
+    if (s < S) len = cu[s + 1] - cu[s];
+    const int units = units_of_seq<QG>(len, B, upb);
+    int incl = units;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int total = __shfl(incl, 63);
+    if (u < base + total) {
+      const bool mine = units > 0 && (base + incl - units) <= u && u < base + incl;
+      const unsigned long long m = __ballot(mine);
+      const int src = __ffsll((long long)m) - 1;
+      const int seq = c0 + src;
+      const int v = u - (base + __shfl(incl - units, src));
+      const int slen = __shfl(len, src);
+      const int nb = (slen - 1) / B + 1;
+      int j = v / upb;
+      if (j > nb - 1) j = nb - 1;
+      const int g = v - j * upb;
+      out.row0 = cu[seq] + j * B;
+      out.L = (j < nb - 1) ? B : slen - (nb - 1) * B;
+      out.q0 = g * QG;
+      out.qn = min(QG, out.L - out.q0);
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+// Upper bound on the number of units of N rows in S sequences:
+// sum_s ceil(len_s/B) <= N/B + S, plus N/QG more query groups when B > QG.
+inline int attn_unit_bound(long long N, int S, int B, int QG) {
+  long long b = N / B + S;
+  if (B > QG) b += N / QG;
+  return (int)b;
+}
+
+}  // namespace gs

@@ -1,0 +1,262 @@
+// gsattn_api.hip -- the C ABI of libgsattn (declared in include/gsattn.h):
+// host-side argument checks, workspace layout and kernel launches.
+//
+// Every check happens before anything is enqueued; on failure the call
+// returns a status and a thread-local detail string and leaves the stream
+// untouched.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "gsattn.h"
+#include "attn_units.hpp"
+
+namespace gs {
+hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int M, int d,
+                                hipStream_t stream);
+hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
+                                int d, hipStream_t stream);
+hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long long N, int d,
+                                  int heads, int B, void* o, hipStream_t stream);
+hipError_t launch_qkv_proj_f32(const void* x, const void* wqkv, void* qkv, int M, int d,
+                               hipStream_t stream);
+hipError_t launch_out_proj_f32(const void* o, const void* wo, const void* x, void* out, int M,
+                               int d, hipStream_t stream);
+hipError_t launch_block_attn_f32(const void* qkv, const int* cu, int S, long long N, int d,
+                                 int heads, int B, void* o, hipStream_t stream);
+
+// Validates cu_seqlens on the device: flag[0] = 0 if cu[0] == 0, cu is
+// non-decreasing and cu[S] == N; 1 otherwise.  One workgroup.
+__global__ void check_cu_kernel(const int* cu, int S, long long N, int* flag) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = (cu[0] != 0) || ((long long)cu[S] != N);
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += blockDim.x)
+    if (cu[s + 1] < cu[s]) atomicOr(&bad, 1);
+  __syncthreads();
+  if (threadIdx.x == 0) flag[0] = bad;
+}
+}  // namespace gs
+
+namespace {
+
+constexpr int kDh = 128;
+constexpr int kMaxD = 8192;
+constexpr size_t kAlign = 256;
+
+thread_local char g_detail[512] = "";
+
+gs_status fail(gs_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(gs_dtype t) { return t == GS_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool debug_checks() {
+  const char* e = getenv("GSATTN_DEBUG_CHECKS");
+  return e && e[0] == '1';
+}
+
+gs_status check_dtype(gs_dtype t) {
+  if (t != GS_F32 && t != GS_BF16) return fail(GS_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)t);
+  return GS_OK;
+}
+
+gs_status check_dims(int64_t N, int32_t d) {
+  if (N < 0) return fail(GS_ERR_INVALID_ARGUMENT, "total_frames %lld < 0", (long long)N);
+  if (N >= (int64_t)1 << 31)
+    return fail(GS_ERR_UNSUPPORTED, "total_frames %lld >= 2^31", (long long)N);
+  if (d < 1) return fail(GS_ERR_INVALID_ARGUMENT, "d_model %d < 1", d);
+  if (d % kDh != 0 || d > kMaxD)
+    return fail(GS_ERR_UNSUPPORTED, "d_model %d: the kernels need a multiple of 128, at most %d",
+                d, kMaxD);
+  if ((__int128)N * 3 * d >= ((__int128)1 << 62))
+    return fail(GS_ERR_UNSUPPORTED, "N * 3d overflows");
+  return GS_OK;
+}
+
+gs_status check_heads(int32_t d, int32_t heads) {
+  if (heads < 1) return fail(GS_ERR_INVALID_ARGUMENT, "heads %d < 1", heads);
+  if (d % heads != 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "d_model %d is not divisible by heads %d", d, heads);
+  if (d / heads != kDh)
+    return fail(GS_ERR_UNSUPPORTED, "head dim %d: the kernels implement dh = 128", d / heads);
+  return GS_OK;
+}
+
+gs_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(GS_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(GS_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return GS_OK;
+}
+
+gs_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GS_OK;
+  return fail(GS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define GS_TRY(expr)             \
+  do {                           \
+    gs_status _s = (expr);       \
+    if (_s != GS_OK) return _s;  \
+  } while (0)
+
+// Runs the device check of cu_seqlens when GSATTN_DEBUG_CHECKS=1.  Needs one
+// int of device scratch.
+gs_status debug_check_cu(const int32_t* cu, int32_t S, int64_t N, int* dflag, hipStream_t st) {
+  if (!debug_checks()) return GS_OK;
+  hipLaunchKernelGGL(gs::check_cu_kernel, dim3(1), dim3(256), 0, st, (const int*)cu, (int)S,
+                     (long long)N, dflag);
+  GS_TRY(hip_status(hipGetLastError(), "cu_seqlens check launch"));
+  int flag = 1;
+  GS_TRY(hip_status(hipMemcpyAsync(&flag, dflag, sizeof(int), hipMemcpyDeviceToHost, st),
+                    "cu_seqlens check copy"));
+  GS_TRY(hip_status(hipStreamSynchronize(st), "cu_seqlens check sync"));
+  if (flag) return fail(GS_ERR_INVALID_ARGUMENT, "cu_seqlens is not a valid offset array");
+  return GS_OK;
+}
+
+gs_status record(const gs_mhsa_desc* desc, int i, hipStream_t st) {
+  if (!desc->kernel_events) return GS_OK;
+  return hip_status(hipEventRecord(desc->kernel_events[i], st), "hipEventRecord");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gs_version(void) { return 10000; }
+
+const char* gs_status_string(gs_status s) {
+  switch (s) {
+    case GS_OK: return "GS_OK";
+    case GS_ERR_INVALID_ARGUMENT: return "GS_ERR_INVALID_ARGUMENT";
+    case GS_ERR_UNSUPPORTED: return "GS_ERR_UNSUPPORTED";
+    case GS_ERR_WORKSPACE_TOO_SMALL: return "GS_ERR_WORKSPACE_TOO_SMALL";
+    case GS_ERR_HIP: return "GS_ERR_HIP";
+  }
+  return "unknown gs_status";
+}
+
+const char* gs_last_error_detail(void) { return g_detail; }
+
+size_t gs_block_mhsa_workspace_bytes(int64_t total_frames, int32_t d_model, gs_dtype dtype) {
+  if (total_frames < 0 || d_model < 1 || (dtype != GS_F32 && dtype != GS_BF16)) return 0;
+  const size_t e = elem_size(dtype);
+  const size_t n = (size_t)total_frames, d = (size_t)d_model;
+  // Q|K|V [N][3d], O [N][d], one aligned slot for the debug flag
+  return align_up(n * 3 * d * e) + align_up(n * d * e) + kAlign;
+}
+
+gs_status gs_qkv_proj(const void* x, const void* Wqkv, void* qkv, int64_t total_frames,
+                      int32_t d_model, gs_dtype dtype, hipStream_t stream) {
+  GS_TRY(check_dtype(dtype));
+  GS_TRY(check_dims(total_frames, d_model));
+  if (total_frames == 0) return GS_OK;
+  GS_TRY(check_ptr(x, "x"));
+  GS_TRY(check_ptr(Wqkv, "Wqkv"));
+  GS_TRY(check_ptr(qkv, "qkv"));
+  const int M = (int)total_frames;
+  hipError_t e = dtype == GS_BF16 ? gs::launch_qkv_proj_bf16(x, Wqkv, qkv, M, d_model, stream)
+                                  : gs::launch_qkv_proj_f32(x, Wqkv, qkv, M, d_model, stream);
+  return hip_status(e, "qkv_proj launch");
+}
+
+gs_status gs_block_attn(const void* qkv, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int64_t total_frames, int32_t d_model, int32_t heads,
+                        int32_t block_frames, gs_dtype dtype, void* o, hipStream_t stream) {
+  GS_TRY(check_dtype(dtype));
+  GS_TRY(check_dims(total_frames, d_model));
+  GS_TRY(check_heads(d_model, heads));
+  if (num_seqs < 1) return fail(GS_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", num_seqs);
+  if (block_frames < 1) return fail(GS_ERR_INVALID_ARGUMENT, "block_frames %d < 1", block_frames);
+  if (!cu_seqlens) return fail(GS_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  if (total_frames == 0) return GS_OK;
+  GS_TRY(check_ptr(qkv, "qkv"));
+  GS_TRY(check_ptr(o, "o"));
+  const long long N = total_frames;
+  hipError_t e =
+      dtype == GS_BF16
+          ? gs::launch_block_attn_bf16(qkv, cu_seqlens, num_seqs, N, d_model, heads, block_frames, o, stream)
+          : gs::launch_block_attn_f32(qkv, cu_seqlens, num_seqs, N, d_model, heads, block_frames, o, stream);
+  return hip_status(e, "block_attn launch");
+}
+
+gs_status gs_out_proj_residual(const void* o, const void* Wo, const void* x, void* out,
+                               int64_t total_frames, int32_t d_model, gs_dtype dtype,
+                               hipStream_t stream) {
+  GS_TRY(check_dtype(dtype));
+  GS_TRY(check_dims(total_frames, d_model));
+  if (total_frames == 0) return GS_OK;
+  GS_TRY(check_ptr(o, "o"));
+  GS_TRY(check_ptr(Wo, "Wo"));
+  GS_TRY(check_ptr(x, "x"));
+  GS_TRY(check_ptr(out, "out"));
+  const int M = (int)total_frames;
+  hipError_t e = dtype == GS_BF16 ? gs::launch_out_proj_bf16(o, Wo, x, out, M, d_model, stream)
+                                  : gs::launch_out_proj_f32(o, Wo, x, out, M, d_model, stream);
+  return hip_status(e, "out_proj launch");
+}
+
+gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void* Wqkv,
+                            const void* Wo, int32_t block_frames, int32_t heads, void* out,
+                            hipStream_t stream, const gs_mhsa_desc* desc) {
+  if (!desc) return fail(GS_ERR_INVALID_ARGUMENT, "desc is NULL");
+  GS_TRY(check_dtype(desc->dtype));
+  const int64_t N = desc->total_frames;
+  const int32_t d = desc->d_model;
+  GS_TRY(check_dims(N, d));
+  GS_TRY(check_heads(d, heads));
+  if (desc->num_seqs < 1) return fail(GS_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", desc->num_seqs);
+  if (block_frames < 1) return fail(GS_ERR_INVALID_ARGUMENT, "block_frames %d < 1", block_frames);
+  if (!cu_seqlens) return fail(GS_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  if (N == 0) return GS_OK;
+  GS_TRY(check_ptr(x, "x"));
+  GS_TRY(check_ptr(Wqkv, "Wqkv"));
+  GS_TRY(check_ptr(Wo, "Wo"));
+  GS_TRY(check_ptr(out, "out"));
+  const size_t e = elem_size(desc->dtype);
+  const size_t xbytes = (size_t)N * d * e;
+  if (out != x) {
+    const char* a = (const char*)x;
+    const char* b = (const char*)out;
+    if (a < b + xbytes && b < a + xbytes)
+      return fail(GS_ERR_INVALID_ARGUMENT, "out partially overlaps x");
+  }
+  const size_t need = gs_block_mhsa_workspace_bytes(N, d, desc->dtype);
+  if (!desc->workspace) return fail(GS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (((uintptr_t)desc->workspace & (kAlign - 1)) != 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (desc->workspace_bytes < need)
+    return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                desc->workspace_bytes, need);
+
+  char* ws = (char*)desc->workspace;
+  void* qkv = ws;
+  void* o = ws + align_up((size_t)N * 3 * d * e);
+  int* dflag = (int*)(ws + align_up((size_t)N * 3 * d * e) + align_up((size_t)N * d * e));
+  GS_TRY(debug_check_cu(cu_seqlens, desc->num_seqs, N, dflag, stream));
+
+  GS_TRY(record(desc, 0, stream));
+  GS_TRY(gs_qkv_proj(x, Wqkv, qkv, N, d, desc->dtype, stream));
+  GS_TRY(record(desc, 1, stream));
+  GS_TRY(gs_block_attn(qkv, cu_seqlens, desc->num_seqs, N, d, heads, block_frames, desc->dtype, o,
+                       stream));
+  GS_TRY(record(desc, 2, stream));
+  GS_TRY(gs_out_proj_residual(o, Wo, x, out, N, d, desc->dtype, stream));
+  GS_TRY(record(desc, 3, stream));
+  return GS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,232 @@
+"""Python binding of libgsattn (ctypes).  Argument marshalling only.
+
+Every step of the sub-layer runs in the library's HIP kernels; PyTorch only
+provides device memory and the current stream.  The names follow the C ABI in
+include/gsattn.h.  If the library is missing the calls raise: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("GSATTN_LIB", os.path.join(HERE, "libgsattn.so"))
+
+GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE_TOO_SMALL, GS_ERR_HIP = range(5)
+GS_F32, GS_BF16 = 0, 1
+
+EXPORTS = (
+    "gs_block_mhsa_workspace_bytes", "gs_block_mhsa_fwd", "gs_qkv_proj", "gs_block_attn",
+    "gs_out_proj_residual", "gs_status_string", "gs_last_error_detail", "gs_version",
+)
+
+
+class GsError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_frames", ctypes.c_int64),
+        ("d_model", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("kernel_events", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """The loaded library (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"libgsattn not built: {p} is missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.gs_block_mhsa_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_block_mhsa_workspace_bytes.argtypes = [I64, I32, ctypes.c_int]
+    lib.gs_block_mhsa_fwd.restype = ctypes.c_int
+    lib.gs_block_mhsa_fwd.argtypes = [P, P, P, P, I32, I32, P, P, ctypes.POINTER(_Desc)]
+    lib.gs_qkv_proj.restype = ctypes.c_int
+    lib.gs_qkv_proj.argtypes = [P, P, P, I64, I32, ctypes.c_int, P]
+    lib.gs_block_attn.restype = ctypes.c_int
+    lib.gs_block_attn.argtypes = [P, P, I32, I64, I32, I32, I32, ctypes.c_int, P, P]
+    lib.gs_out_proj_residual.restype = ctypes.c_int
+    lib.gs_out_proj_residual.argtypes = [P, P, P, P, I64, I32, ctypes.c_int, P]
+    lib.gs_status_string.restype = ctypes.c_char_p
+    lib.gs_status_string.argtypes = [ctypes.c_int]
+    lib.gs_last_error_detail.restype = ctypes.c_char_p
+    lib.gs_last_error_detail.argtypes = []
+    lib.gs_version.restype = ctypes.c_int32
+    lib.gs_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != GS_OK:
+        lib = load()
+        raise GsError(status, lib.gs_status_string(status).decode(),
+                      lib.gs_last_error_detail().decode())
+
+
+def _gs_dtype(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return GS_BF16
+    if t == torch.float32:
+        return GS_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype: Optional[torch.dtype] = None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def workspace_bytes(total_frames: int, d_model: int, dtype: torch.dtype) -> int:
+    return int(load().gs_block_mhsa_workspace_bytes(int(total_frames), int(d_model), _gs_dtype(dtype)))
+
+
+def alloc_workspace(total_frames: int, d_model: int, dtype: torch.dtype, device=None) -> torch.Tensor:
+    n = workspace_bytes(total_frames, d_model, dtype)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def block_mhsa_fwd(x: torch.Tensor, cu_seqlens: torch.Tensor, wqkv: torch.Tensor, wo: torch.Tensor,
+                   block_frames: int, heads: int, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   kernel_events: Optional["HipEvents"] = None) -> torch.Tensor:
+    """out = x + BlockMHSA(x), enqueued on `stream` (default: torch's current stream)."""
+    lib = load()
+    n, d = x.shape
+    dt = _gs_dtype(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(n, d, x.dtype, x.device)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    desc = _Desc(int(cu_seqlens.numel()) - 1, int(n), int(d), dt, workspace.data_ptr(),
+                 int(workspace.numel()), kernel_events.handle_array() if kernel_events else None)
+    _check(lib.gs_block_mhsa_fwd(
+        _dev(x, "x"), _dev(cu_seqlens, "cu_seqlens"), _dev(wqkv, "Wqkv", x.dtype),
+        _dev(wo, "Wo", x.dtype), int(block_frames), int(heads), _dev(out, "out", x.dtype),
+        _stream(stream), ctypes.byref(desc)))
+    return out
+
+
+def qkv_proj(x: torch.Tensor, wqkv: torch.Tensor, qkv: Optional[torch.Tensor] = None, stream=None):
+    n, d = x.shape
+    if qkv is None:
+        qkv = torch.empty((n, 3 * d), dtype=x.dtype, device=x.device)
+    _check(load().gs_qkv_proj(_dev(x, "x"), _dev(wqkv, "Wqkv", x.dtype), _dev(qkv, "qkv", x.dtype),
+                              int(n), int(d), _gs_dtype(x.dtype), _stream(stream)))
+    return qkv
+
+
+def block_attn(qkv: torch.Tensor, cu_seqlens: torch.Tensor, heads: int, block_frames: int,
+               o: Optional[torch.Tensor] = None, stream=None):
+    n, d3 = qkv.shape
+    d = d3 // 3
+    if o is None:
+        o = torch.empty((n, d), dtype=qkv.dtype, device=qkv.device)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check(load().gs_block_attn(_dev(qkv, "qkv"), _dev(cu_seqlens, "cu_seqlens"),
+                                int(cu_seqlens.numel()) - 1, int(n), int(d), int(heads),
+                                int(block_frames), _gs_dtype(qkv.dtype), _dev(o, "o", qkv.dtype),
+                                _stream(stream)))
+    return o
+
+
+def out_proj_residual(o: torch.Tensor, wo: torch.Tensor, x: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, stream=None):
+    n, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(load().gs_out_proj_residual(_dev(o, "o", x.dtype), _dev(wo, "Wo", x.dtype), _dev(x, "x"),
+                                       _dev(out, "out", x.dtype), int(n), int(d),
+                                       _gs_dtype(x.dtype), _stream(stream)))
+    return out
+
+
+class HipEvents:
+    """A few raw hipEvent_t handles (for the library's per-kernel timing hook)."""
+
+    def __init__(self, count: int = 4):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._arr = (ctypes.c_void_p * count)()
+        for i in range(count):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self._arr[i] = h
+        self.count = count
+
+    def handle_array(self, offset: int = 0) -> int:
+        """Address of the hipEvent_t array starting at event `offset`."""
+        if not 0 <= offset < self.count:
+            raise IndexError(offset)
+        return ctypes.addressof(self._arr) + offset * ctypes.sizeof(ctypes.c_void_p)
+
+    def view(self, offset: int) -> "_EventView":
+        """The events offset..offset+3, as the library's four timing events."""
+        if offset + 4 > self.count:
+            raise IndexError(offset)
+        return _EventView(self, offset)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        """Milliseconds between events i and j (waits for j)."""
+        if self._hip.hipEventSynchronize(self._arr[j]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self._arr[i], self._arr[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            for i in range(self.count):
+                self._hip.hipEventDestroy(self._arr[i])
+        except Exception:
+            pass
+
+
+class _EventView:
+    def __init__(self, events: HipEvents, offset: int):
+        self.events, self.offset = events, offset
+
+    def handle_array(self) -> int:
+        return self.events.handle_array(self.offset)

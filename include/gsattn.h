@@ -1,0 +1,137 @@
+/*
+ * gsattn.h -- C ABI of libgsattn: the block-local multi-head self-attention
+ * sub-layer of the Granite-Speech-4.1-2B-NAR conformer encoder on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (IBM model card, "Model Architecture" (1) CTC Speech Encoder:
+ * every conformer layer uses block attention with 4-second audio blocks; the
+ * card's usage section runs it with sequence packing and non-causal,
+ * i.e. bidirectional, attention):
+ *
+ *   given packed rows x[N][d] of S sequences delimited by cu_seqlens[S+1],
+ *     qkv = x . Wqkv^T                           (Wqkv [3d][d], rows Q|K|V)
+ *     for every block of at most B consecutive rows of one sequence
+ *       (blocks restart at each sequence's first row, the last block of a
+ *        sequence holds the remainder) and every head h (dh = d / heads):
+ *       O_h = softmax(Q_h K_h^T / sqrt(dh)) V_h  (no mask inside the block)
+ *     out = x + O . Wo^T                         (Wo [d][d], O in head order)
+ *
+ * No bias, normalisation or positional term belongs to this sub-layer.
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers named x, Wqkv, Wo, out, qkv, o, workspace, cu_seqlens are
+ *     DEVICE pointers, owned by the caller; the library allocates nothing.
+ *   - Row-major, densely packed.  Weights use the nn.Linear [out][in] layout;
+ *     inside Wqkv rows 0..d-1 are Q, d..2d-1 are K, 2d..3d-1 are V, and head
+ *     h owns rows h*dh..h*dh+dh-1 of each.  O columns are head-concatenated.
+ *   - dtype GS_BF16: x, weights, out and intermediates are bfloat16, all sums
+ *     accumulate in fp32, every fp32->bf16 conversion rounds to nearest even.
+ *     GS_F32: everything IEEE fp32.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Supported on the GPU: dh == 128 (d = 128 * heads), d_model <= 8192,
+ *     total_frames < 2^31.  Other shapes return GS_ERR_UNSUPPORTED.
+ *   - Work is enqueued on `stream` and the call returns without waiting;
+ *     device faults surface at the caller's next synchronisation.
+ *   - Argument errors are detected on the host before anything is enqueued,
+ *     so a non-OK status means no device work was issued (except GS_ERR_HIP,
+ *     reported when a launch itself fails).
+ *   - cu_seqlens (int32, S+1 entries) must satisfy cu[0] = 0, cu[s] <= cu[s+1],
+ *     cu[S] = total_frames.  It lives on the device and is not read by the
+ *     host; violating it is undefined behaviour unless the environment
+ *     variable GSATTN_DEBUG_CHECKS=1 is set, which validates it on the device
+ *     (with a stream synchronisation) before launching.
+ */
+#ifndef GSATTN_H
+#define GSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GS_OK = 0,
+  GS_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misaligned pointer, bad cu_seqlens */
+  GS_ERR_UNSUPPORTED = 2,        /* valid, but not a shape the GPU kernels implement */
+  GS_ERR_WORKSPACE_TOO_SMALL = 3,
+  GS_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} gs_status;
+
+typedef enum { GS_F32 = 0, GS_BF16 = 1 } gs_dtype;
+
+/* Sizes and scratch for gs_block_mhsa_fwd. */
+typedef struct {
+  int32_t num_seqs;        /* S >= 1; cu_seqlens has S+1 entries */
+  int64_t total_frames;    /* N = cu_seqlens[S] >= 0 (N == 0 is a no-op) */
+  int32_t d_model;         /* d */
+  gs_dtype dtype;
+  void* workspace;         /* device scratch, >= gs_block_mhsa_workspace_bytes() bytes,
+                              256-byte aligned; holds Q|K|V [N][3d] then O [N][d] */
+  size_t workspace_bytes;
+  /* Optional (may be NULL): four events the library records on `stream`
+     before the projection kernel, after it, after the attention kernel and
+     after the output-projection kernel, for per-kernel timing. */
+  hipEvent_t* kernel_events;
+} gs_mhsa_desc;
+
+/* Bytes of workspace gs_block_mhsa_fwd needs for these sizes (0 on bad input). */
+size_t gs_block_mhsa_workspace_bytes(int64_t total_frames, int32_t d_model, gs_dtype dtype);
+
+/*
+ * The whole sub-layer: out = x + BlockMHSA(x).
+ *   x          [N][d]    input rows (packed sequences)
+ *   cu_seqlens [S+1]     int32 sequence offsets (device)
+ *   Wqkv       [3d][d]   projection weights
+ *   Wo         [d][d]    output projection weights
+ *   block_frames          B >= 1; B >= the longest sequence gives full attention
+ *   heads                 number of heads, d % heads == 0
+ *   out        [N][d]    result; may equal x (in place); any other overlap is invalid
+ *   stream               HIP stream to enqueue on (0 = null stream)
+ *   desc                 sizes, dtype, workspace (see gs_mhsa_desc)
+ * Three kernels run in stream order: projection, block attention, output
+ * projection with the residual.
+ */
+gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void* Wqkv,
+                            const void* Wo, int32_t block_frames, int32_t heads, void* out,
+                            hipStream_t stream, const gs_mhsa_desc* desc);
+
+/*
+ * Step 1 alone: qkv[N][3d] = x[N][d] . Wqkv[3d][d]^T (fp32 accumulate).
+ */
+gs_status gs_qkv_proj(const void* x, const void* Wqkv, void* qkv, int64_t total_frames,
+                      int32_t d_model, gs_dtype dtype, hipStream_t stream);
+
+/*
+ * Step 2 alone: o[N][d] from qkv[N][3d] (layout as produced by gs_qkv_proj):
+ * per block and head, softmax(Q K^T / sqrt(dh)) V, keys limited to the block.
+ */
+gs_status gs_block_attn(const void* qkv, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int64_t total_frames, int32_t d_model, int32_t heads,
+                        int32_t block_frames, gs_dtype dtype, void* o, hipStream_t stream);
+
+/*
+ * Step 3 alone: out[N][d] = x[N][d] + o[N][d] . Wo[d][d]^T (fp32 accumulate and
+ * add, one rounding).  out may equal x.
+ */
+gs_status gs_out_proj_residual(const void* o, const void* Wo, const void* x, void* out,
+                               int64_t total_frames, int32_t d_model, gs_dtype dtype,
+                               hipStream_t stream);
+
+/* Static text for a status code. */
+const char* gs_status_string(gs_status s);
+
+/* Thread-local detail for the last non-OK status returned on this thread. */
+const char* gs_last_error_detail(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t gs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSATTN_H */

@@ -1,0 +1,104 @@
+"""The C-ABI library loads and exports what include/gsattn.h declares; host-side
+checks reject bad arguments before any device work (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conformer_block_attention_amd import gsattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsattn.h")
+
+FAKE = 0x10000  # a non-null, 256-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gs_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gsattn.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(gsattn.EXPORTS) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gs_version() >= 10000
+    for code, name in enumerate(["GS_OK", "GS_ERR_INVALID_ARGUMENT", "GS_ERR_UNSUPPORTED",
+                                 "GS_ERR_WORKSPACE_TOO_SMALL", "GS_ERR_HIP"]):
+        assert lib.gs_status_string(code).decode() == name
+
+
+def test_workspace_bytes(lib):
+    n, d = 1000, 1024
+    for dt, e in ((gsattn.GS_BF16, 2), (gsattn.GS_F32, 4)):
+        got = lib.gs_block_mhsa_workspace_bytes(n, d, dt)
+        al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+        assert got == al(n * 3 * d * e) + al(n * d * e) + 256
+    assert lib.gs_block_mhsa_workspace_bytes(-1, d, gsattn.GS_BF16) == 0
+    assert lib.gs_block_mhsa_workspace_bytes(n, d, 7) == 0
+
+
+def _desc(S=2, N=400, d=1024, dt=gsattn.GS_BF16, ws=FAKE, wsb=1 << 40):
+    return gsattn._Desc(S, N, d, dt, ws, wsb, None)
+
+
+def _fwd(lib, desc, x=FAKE, cu=FAKE, wqkv=FAKE, wo=FAKE, B=200, H=8, out=FAKE + (1 << 30)):
+    d = ctypes.byref(desc) if desc is not None else None
+    st = lib.gs_block_mhsa_fwd(x, cu, wqkv, wo, B, H, out, None, d)
+    return st, lib.gs_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("kw,desc_kw,code", [
+    ({}, None, gsattn.GS_ERR_INVALID_ARGUMENT),                       # desc NULL
+    ({"x": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"cu": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"wqkv": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"wo": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"out": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"x": FAKE + 2}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),            # misaligned
+    ({"B": 0}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"H": 0}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"H": 3}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),                   # 1024 % 3
+    ({"H": 16}, {}, gsattn.GS_ERR_UNSUPPORTED),                       # dh = 64
+    ({}, {"S": 0}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"N": -5}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"d": 1000}, gsattn.GS_ERR_UNSUPPORTED),
+    ({}, {"dt": 9}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"ws": None}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"ws": FAKE + 16}, gsattn.GS_ERR_INVALID_ARGUMENT),          # workspace alignment
+    ({}, {"wsb": 1000}, gsattn.GS_ERR_WORKSPACE_TOO_SMALL),
+    ({"out": FAKE + 4096}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),       # partial overlap with x
+])
+def test_argument_errors(lib, kw, desc_kw, code):
+    desc = None if desc_kw is None else _desc(**desc_kw)
+    st, detail = _fwd(lib, desc, **kw)
+    assert st == code, (st, detail)
+    assert detail
+
+
+def test_empty_input_is_noop(lib):
+    # N = 0 returns before touching any pointer or the device
+    st, _ = _fwd(lib, _desc(N=0, ws=None, wsb=0), x=None, wqkv=None, wo=None, out=None)
+    assert st == gsattn.GS_OK
+
+
+def test_stage_argument_errors(lib):
+    assert lib.gs_qkv_proj(None, FAKE, FAKE, 10, 1024, gsattn.GS_BF16, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_qkv_proj(FAKE, FAKE, FAKE, 10, 96, gsattn.GS_BF16, None) == gsattn.GS_ERR_UNSUPPORTED
+    assert lib.gs_block_attn(FAKE, FAKE, 0, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_block_attn(FAKE, None, 1, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_block_attn(FAKE, FAKE, 1, 10, 1024, 8, 0, gsattn.GS_BF16, FAKE, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_out_proj_residual(FAKE, FAKE, None, FAKE, 10, 1024, gsattn.GS_F32, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_qkv_proj(FAKE, FAKE, FAKE, 1 << 31, 1024, gsattn.GS_BF16, None) == gsattn.GS_ERR_UNSUPPORTED

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (max-abs error relative to the RMS of the oracle's output): 1e-4
+for the fp32 path and 2e-2 for the bf16 path against the fp64 oracle fed the
+same bf16 values.
+"""
+import numpy as np
+import pytest
+import torch
+
+from conformer_block_attention_amd import gsattn, workloads
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_case(case, tol=None, orc=None):
+    x, cu, wqkv, wo = G.on_dev(case)
+    out = G.run(x, cu, wqkv, wo, case.block_frames, case.heads)
+    ref = orc.block_mhsa(case.x, case.cu, case.weights[0][0], case.weights[0][1],
+                         case.block_frames, case.heads)
+    err = G.rel_err(out.double().cpu().numpy(), ref)
+    t = G.tol_for(case.dtype) if tol is None else tol
+    print(f"  err={err:.3e} tol={t:g}", flush=True)
+    assert err <= t, err
+    return out, ref
+
+
+# ---------------------------------------------------------------------------
+# single steps (same inputs on both sides), each against an a-priori bound on
+# the error of its rounding points:
+#   bf16 output rounding (RNE):  |fl(v) - v| <= u |v|, u = 2^-8
+#   fp32 accumulation of K products, any order: <= K * 2^-24 * sum |a_k b_k|
+#   P rounded to bf16 before the PV product (softmax weights w, values v):
+#     |o~ - o| <= u * sum_l w_l |v_l - o|  (first order)
+
+U_BF16 = 2.0 ** -8
+U_F32 = 2.0 ** -24
+
+
+def _gemm_bound(a, b, ref, dtype):
+    """|fl(ref) - ref| bound for ref = a . b^T (+ residual) with fp32 accumulation."""
+    acc = a.shape[1] * U_F32 * (np.abs(a) @ np.abs(b).T)
+    out_round = (U_BF16 if dtype == torch.bfloat16 else U_F32) * np.abs(ref)
+    return 1.01 * (acc + out_round) + 1e-30
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_stage_qkv_proj(orc, dtype):
+    G.print_case("stage_qkv_proj", dtype=dtype)
+    case = workloads.custom_case([300, 77], 1024, 8, 200, dtype, seed=1)
+    x, _, wqkv, _ = G.on_dev(case)
+    qkv = gsattn.qkv_proj(x, wqkv)
+    torch.cuda.synchronize()
+    ref = orc.qkv_proj(case.x, case.weights[0][0])
+    got = qkv.double().cpu().numpy()
+    bound = _gemm_bound(case.x.double().numpy(), case.weights[0][0].double().numpy(), ref, dtype)
+    worst = float(np.max(np.abs(got - ref) / bound))
+    print(f"  worst error / bound = {worst:.3f}", flush=True)
+    assert worst <= 1.0, worst
+
+
+def _attn_bound(qkv, cu, heads, B, o_ref, dtype):
+    """Per-element first-order bound for the attention step (numpy, brute force):
+    P rounding + logit error + fp32 PV accumulation + output rounding."""
+    n, d3 = qkv.shape
+    d = d3 // 3
+    dh = d // heads
+    bf = dtype == torch.bfloat16
+    u_p = U_BF16 if bf else 4 * U_F32        # P rounded to bf16 / exp2 in fp32
+    u_o = U_BF16 if bf else U_F32            # final rounding of O
+    bound = np.zeros((n, d))
+    for s in range(len(cu) - 1):
+        for a in range(int(cu[s]), int(cu[s + 1]), B):
+            e = min(a + B, int(cu[s + 1]))
+            L = e - a
+            for h in range(heads):
+                q = qkv[a:e, h * dh:(h + 1) * dh]
+                k = qkv[a:e, d + h * dh:d + (h + 1) * dh]
+                v = qkv[a:e, 2 * d + h * dh:2 * d + (h + 1) * dh]
+                z = q @ k.T / np.sqrt(dh)
+                w = np.exp(z - z.max(axis=1, keepdims=True))
+                w /= w.sum(axis=1, keepdims=True)
+                zerr = (dh + 4) * U_F32 * (np.abs(q) @ np.abs(k).T) / np.sqrt(dh) + 4 * U_F32 * np.abs(z)
+                o = o_ref[a:e, h * dh:(h + 1) * dh]
+                dev = np.abs(v[None, :, :] - o[:, None, :])          # |v_l - o_i|
+                spread = np.einsum("il,ile->ie", w * (u_p + zerr), dev)
+                pv_acc = (L + 2) * U_F32 * (w @ np.abs(v))
+                bound[a:e, h * dh:(h + 1) * dh] = spread + pv_acc + u_o * np.abs(o)
+    return 1.05 * bound + 1e-30
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("lengths,B", [([200, 200, 22], 200), ([1, 17, 64, 65, 130], 64),
+                                       ([700, 3], 600), ([5, 0, 9], 1)])
+def test_stage_block_attn(orc, dtype, lengths, B):
+    G.print_case("stage_block_attn", dtype=dtype, lengths=lengths, B=B)
+    d, H = 256, 2
+    n = int(np.sum(lengths))
+    g = torch.Generator().manual_seed(5)
+    qkv_cpu = torch.randn(n, 3 * d, generator=g).to(dtype)
+    cu = workloads.cu_seqlens(lengths)
+    o = gsattn.block_attn(qkv_cpu.to(G.dev()), torch.from_numpy(cu).to(G.dev()), H, B)
+    torch.cuda.synchronize()
+    ref = orc.block_attn(qkv_cpu, cu, H, B)
+    got = o.double().cpu().numpy()
+    bound = _attn_bound(qkv_cpu.double().numpy(), cu, H, B, ref, dtype)
+    worst = float(np.max(np.abs(got - ref) / bound))
+    print(f"  worst error / bound = {worst:.3f}", flush=True)
+    assert worst <= 1.0, worst
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_stage_out_proj(orc, dtype):
+    G.print_case("stage_out_proj", dtype=dtype)
+    case = workloads.custom_case([333], 1024, 8, 200, dtype, seed=2)
+    g = torch.Generator().manual_seed(3)
+    o_cpu = torch.randn(333, 1024, generator=g).to(dtype)
+    x, _, _, wo = G.on_dev(case)
+    out = gsattn.out_proj_residual(o_cpu.to(G.dev()), wo, x)
+    torch.cuda.synchronize()
+    ref = orc.out_proj_residual(o_cpu, case.weights[0][1], case.x)
+    got = out.double().cpu().numpy()
+    bound = _gemm_bound(o_cpu.double().numpy(), case.weights[0][1].double().numpy(), ref, dtype)
+    bound += 1.01 * U_F32 * np.abs(ref)  # the residual add in fp32
+    worst = float(np.max(np.abs(got - ref) / bound))
+    print(f"  worst error / bound = {worst:.3f}", flush=True)
+    assert worst <= 1.0, worst
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+
+def test_workload_fp32_t422(orc):
+    G.print_case("fp32_t422")
+    _full_case(workloads.build_case(workloads.WORKLOADS["fp32_t422"]), orc=orc)
+
+
+def test_workload_bf16_t800(orc):
+    G.print_case("bf16_t800")
+    _full_case(workloads.build_case(workloads.WORKLOADS["bf16_t800"]), orc=orc)
+
+
+@pytest.mark.parametrize("name", ["bf16_b32_long", "bf16_b128_lognormal"])
+def test_workload_full_size_sampled(orc, name):
+    """Full size, launch configuration of the benchmark; oracle on sampled blocks."""
+    G.print_case(name)
+    case = workloads.build_case(workloads.WORKLOADS[name])
+    x, cu, wqkv, wo = G.on_dev(case)
+    out = G.run(x, cu, wqkv, wo, case.block_frames, case.heads)
+    out2 = G.run(x, cu, wqkv, wo, case.block_frames, case.heads)
+    assert torch.equal(out, out2), "run-to-run results differ"
+    mask = G.sample_mask(case.lengths, case.block_frames, n_random=6, seed=1)
+    ref = orc.block_mhsa(case.x, case.cu, case.weights[0][0], case.weights[0][1],
+                         case.block_frames, case.heads, mask=mask)
+    sel = mask.astype(bool)
+    got = out.double().cpu().numpy()[sel]
+    err = G.rel_err(got, ref[sel])
+    print(f"  sampled rows={int(sel.sum())} err={err:.3e}", flush=True)
+    assert err <= G.BF16_TOL, err
+    # packing invariance on a few sequences: packed rows == that sequence run alone (bitwise)
+    for s in (0, len(case.lengths) // 2, len(case.lengths) - 1):
+        a, b = int(case.cu[s]), int(case.cu[s + 1])
+        one = G.run(x[a:b].contiguous(), torch.tensor([0, b - a], dtype=torch.int32, device=G.dev()),
+                    wqkv, wo, case.block_frames, case.heads)
+        assert torch.equal(one, out[a:b]), f"sequence {s} differs when run alone"
+
+
+# ---------------------------------------------------------------------------
+# ragged and degenerate shapes, element by element
+
+EDGE = [
+    # lengths, B, d, heads
+    ([1], 200, 1024, 8),
+    ([200, 200, 22], 200, 1024, 8),
+    ([199, 201, 1, 0, 16, 17], 200, 256, 2),
+    ([0, 0, 5], 200, 128, 1),
+    ([300, 45], 1, 256, 2),            # B = 1: closed form x + x Wv Wo
+    ([123, 77, 250], 10000, 256, 2),   # B >= every length: full attention
+    ([640, 129], 300, 256, 2),         # B > 256: several query groups per block
+    ([1000], 700, 128, 1),
+    ([33, 64, 65, 127, 128, 129], 64, 512, 4),
+    ([513, 257], 256, 256, 2),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("lengths,B,d,H", EDGE)
+def test_edge_shapes(orc, dtype, lengths, B, d, H):
+    G.print_case("edge", dtype=dtype, lengths=lengths, B=B, d=d, H=H)
+    case = workloads.custom_case(lengths, d, H, B, dtype, seed=sum(lengths) + B)
+    _full_case(case, orc=orc)
+
+
+def test_bf16_more_sequences_than_a_wave(orc):
+    """S > 64 exercises the multi-chunk unit search."""
+    lengths = list(np.random.default_rng(3).integers(0, 40, size=150))
+    G.print_case("many_seqs", S=len(lengths))
+    case = workloads.custom_case(lengths, 256, 2, 16, torch.bfloat16, seed=4)
+    _full_case(case, orc=orc)
+
+
+# ---------------------------------------------------------------------------
+# exact properties of the kernels (no oracle)
+
+def test_wo_zero_gives_identity():
+    case = workloads.custom_case([310, 90], 1024, 8, 200, torch.bfloat16, seed=9)
+    x, cu, wqkv, wo = G.on_dev(case)
+    out = G.run(x, cu, wqkv, torch.zeros_like(wo), 200, 8)
+    assert torch.equal(out, x)
+
+
+def test_power_of_two_rescaling_is_exact():
+    case = workloads.custom_case([250, 170], 1024, 8, 200, torch.bfloat16, seed=10)
+    x, cu, wqkv, wo = G.on_dev(case)
+    w2 = wqkv.clone()
+    w2[:1024] *= 4
+    w2[1024:2048] *= 0.25
+    a = G.run(x, cu, wqkv, wo, 200, 8)
+    b = G.run(x, cu, w2, wo, 200, 8)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_in_place_matches_out_of_place(dtype):
+    case = workloads.custom_case([410, 11], 512, 4, 200, dtype, seed=11)
+    x, cu, wqkv, wo = G.on_dev(case)
+    ref = G.run(x, cu, wqkv, wo, 200, 4)
+    y = x.clone()
+    G.run(y, cu, wqkv, wo, 200, 4, out=y)
+    assert torch.equal(y, ref)
+
+
+def test_block_permutation_equivariance():
+    """Permuting rows inside one block permutes the outputs (bf16: same values up to
+    summation order, so compared with the bf16 tolerance)."""
+    case = workloads.custom_case([200, 200], 1024, 8, 200, torch.bfloat16, seed=12)
+    x, cu, wqkv, wo = G.on_dev(case)
+    ref = G.run(x, cu, wqkv, wo, 200, 8)
+    perm = torch.arange(400, device=G.dev())
+    perm[200:] = 200 + torch.randperm(200, generator=torch.Generator().manual_seed(0)).to(G.dev())
+    got = G.run(x[perm].contiguous(), cu, wqkv, wo, 200, 8)
+    assert torch.equal(got[:200], ref[:200])
+    err = G.rel_err(got[200:].double().cpu().numpy(), ref[perm][200:].double().cpu().numpy())
+    assert err <= G.BF16_TOL, err
+
+
+def test_kernel_events_recorded():
+    case = workloads.custom_case([600, 300], 1024, 8, 200, torch.bfloat16, seed=13)
+    x, cu, wqkv, wo = G.on_dev(case)
+    ev = gsattn.HipEvents(4)
+    G.run(x, cu, wqkv, wo, 200, 8, kernel_events=ev)
+    t = [ev.elapsed_ms(i, i + 1) for i in range(3)]
+    assert all(v > 0 for v in t), t
+
+
+def test_debug_check_rejects_bad_cu_seqlens(monkeypatch):
+    monkeypatch.setenv("GSATTN_DEBUG_CHECKS", "1")
+    case = workloads.custom_case([100, 50], 256, 2, 64, torch.bfloat16, seed=14)
+    x, cu, wqkv, wo = G.on_dev(case)
+    G.run(x, cu, wqkv, wo, 64, 2)  # valid passes
+    bad = torch.tensor([0, 120, 110], dtype=torch.int32, device=G.dev())  # decreasing, wrong end
+    with pytest.raises(gsattn.GsError) as e:
+        gsattn.block_mhsa_fwd(x, bad, wqkv, wo, 64, 2)
+    assert e.value.status == gsattn.GS_ERR_INVALID_ARGUMENT
