@@ -6,273 +6,392 @@
 //   O_h = softmax(Q_h K_h^T / sqrt(128)) V_h
 // reading Q|K|V from the projection output qkv[N][3d] and writing O[N][d].
 //
-// Work unit = (block, group of up to 256 query rows); grid = units x heads.
-// Units are found on the device from cu_seqlens (no host round trip): each
-// wave scans the per-sequence unit counts with a wave prefix sum.  The grid is
-// an upper bound; surplus workgroups exit at once.
+// Work item = (unit, head), unit = (block, group of up to 256 query rows),
+// taken from a unit table built on the device from cu_seqlens (read here with
+// scalar loads).
 //
-// Per workgroup (8 waves, 512 threads):
-//   * each wave owns up to two 16-row query tiles (Q stays in registers as the
-//     MFMA B operand);
-//   * keys stream through LDS in chunks of 64, double buffered: K as
-//     [key][dh] (LDS-direct 16-byte copies) and V transposed to [dh][key]
-//     (through registers), so both MFMA operands are read as 16-byte rows;
-//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16.  The K rows
-//     of each 16-key MFMA tile are permuted so that a lane's scores for two
-//     adjacent tiles are 8 consecutive keys -- exactly the P^T operand layout
-//     of the PV product; P never leaves registers;
+// Persistent workgroups, one per CU (8 waves): workgroup w processes items
+// w, w + G, w + 2G, ...  All operands stream through one LDS ring of NST
+// stages of 16 KB filled by 16-byte global->LDS direct copies: an item
+// contributes its query stages (64 rows each), then its key chunks (32 K
+// rows + 32 V rows).  Copies run NST-1 stages ahead of the math, across item
+// boundaries, so the memory pipe does not drain between items.  Each wave
+// counts its own vector-memory operations, so the wait before a stage allows
+// exactly the operations issued after that stage's copies (later copies and
+// O stores) to stay in flight.
+//
+// Math per wave (32 query rows = two 16-row tiles), v_mfma_f32_16x16x32_bf16:
+//   * S^T = K Q^T: the K rows of the two 16-key tiles of a chunk are permuted
+//     so that a lane's scores for both tiles are 8 consecutive keys -- the P^T
+//     operand layout of the PV product; P never leaves registers;
+//   * O^T += V^T P^T: the V^T operand is read straight from the row-major V
+//     rows with the transposing LDS read ds_read_b64_tr_b16 (per 16-lane
+//     group, lane j receives element j%4 of the 8-byte pieces addressed by
+//     lanes j/4 + 4s, s = 0..3);
 //   * online softmax in base 2 with fp32 running max and sum; the max is
-//     reduced across the 4 lane groups holding the same query, the sum only
-//     at the end.  P is rounded to bf16 (RNE) for the MFMA and the sum uses
-//     the rounded values; O = acc / sum is rounded once to bf16.
-//   * keys past the block end are read from the block's last row (finite
-//     data) and masked to -inf, so no read leaves the block.
+//     reduced across the 4 lane groups holding one query, the sum at the end;
+//     P is rounded to bf16 (RNE) for the MFMA and the sum uses the rounded
+//     values; O = acc / sum is rounded once to bf16;
+//   * rows past the block end are copied from its last row (finite data),
+//     keys past it are masked to -inf, and key tiles or query tiles lying
+//     wholly past the end are skipped.
 #include "attn_units.hpp"
 
 namespace gs {
 
 constexpr int ATT_THREADS = 512;
 constexpr int ATT_WAVES = ATT_THREADS / 64;
-constexpr int ATT_QG = 256;   // query rows per workgroup
-constexpr int ATT_KC = 64;    // keys per LDS chunk
+constexpr int ATT_QG = 256;          // query rows per unit (8 waves x 32)
+constexpr int ATT_QS = 64;           // query rows per query stage
+constexpr int ATT_KC = 32;           // keys per key chunk
 constexpr int DH = 128;
+constexpr int ATT_NST = 8;           // ring stages
+constexpr int STAGE_ELEMS = 8192;    // 16 KB: 64 rows of 128 bf16
+constexpr int COPIES = 2;            // 16-byte copies per lane per stage
 
-// LDS layouts (bf16 elements):
-//   Ks [64 keys][128 dh]  row = 256 B = 16 chunks of 16 B; chunk c of key k is
-//                         stored at physical chunk c ^ fk(k)
-//   Vt [128 dh][64 keys]  row = 128 B = 8 chunks; chunk c of row e is stored at
-//                         c ^ fv(e)
-// fk spreads the 8 keys {0..3, 8..11} (+4, +32) that 8 consecutive lanes read;
-// fv spreads both the 8 consecutive rows the MFMA reads and the rows 4 apart
-// the transposing writes touch.
-__device__ __forceinline__ int fk(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
-__device__ __forceinline__ int fv(int e) { return (e ^ (e >> 2)) & 7; }
+// LDS rows are 128 bf16 = 256 B = 16 chunks of 16 B, one full window of the
+// 64 four-byte banks; chunk c of row r is stored at physical chunk c ^ swz(r)
+// so that each read below touches distinct banks:
+//   Q rows: 16 consecutive rows read at one chunk              -> r & 15
+//   K rows: the 16 permuted keys of an MFMA tile at one chunk,
+//           keys {g*8 + i (+4) : g, i = 0..3}                   -> (k&3) | ((k>>3)&3)<<2
+//   V rows: a transposing read takes a chunk pair of 8 keys
+//           {g*8 + i : g = 0,1; i = 0..3} per half-wave          -> pair ^ ((k&3) | ((k>>3)&1)<<2)
+__device__ __forceinline__ int swz_q(int r) { return r & 15; }
+__device__ __forceinline__ int swz_k(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
+__device__ __forceinline__ int swz_v(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
 
-// Key row (chunk-relative) that row r of 16-key MFMA tile ks feeds: the tile
-// pair (ks/2) covers 32 keys; tile parity selects the upper/lower 4 of each 8.
-__device__ __forceinline__ int perm_key(int ks, int r) {
-  return (ks >> 1) * 32 + (r >> 2) * 8 + (ks & 1) * 4 + (r & 3);
+// Chunk-relative key that row r of 16-key MFMA tile kt feeds.
+__device__ __forceinline__ int perm_key(int kt, int r) {
+  return (kt >> 1) * 32 + (r >> 2) * 8 + (kt & 1) * 4 + (r & 3);
+}
+
+// Two transposing LDS reads (ds_read_b64_tr_b16) and a wait for them, in one
+// asm block so both results are complete when it ends.  (Through the builtin,
+// the compiler makes every such read wait for all in-flight global->LDS
+// copies, which would drain the ring; ordering against those copies is
+// enforced here by the explicit waits and barriers of the stream loop.)
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const GS_LDS bf16* p0, const GS_LDS bf16* p1) {
+  unsigned long long r0, r1;
+  const unsigned a0 = (unsigned)(uintptr_t)p0, a1 = (unsigned)(uintptr_t)p1;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(bf16x8, u64x2{r0, r1});
+}
+
+// Workgroup barrier without a memory fence.  A fence would make every wave
+// wait for all of its outstanding global->LDS copies and global stores; the
+// stream loop instead waits explicitly for exactly the copies it needs.  This
+// wave's own LDS reads are complete before it arrives (wait_lds), and the
+// empty asm with a memory clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void stream_barrier() {
+  wait_lds();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most n of this wave's vector-memory operations are pending
+// (n rounded down to even and capped at 30, which only waits longer).
+#define GS_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n >= 30 ? 15 : (n < 0 ? 0 : n >> 1)) {
+    case 0: GS_VMCNT(0); break;    case 1: GS_VMCNT(2); break;
+    case 2: GS_VMCNT(4); break;    case 3: GS_VMCNT(6); break;
+    case 4: GS_VMCNT(8); break;    case 5: GS_VMCNT(10); break;
+    case 6: GS_VMCNT(12); break;   case 7: GS_VMCNT(14); break;
+    case 8: GS_VMCNT(16); break;   case 9: GS_VMCNT(18); break;
+    case 10: GS_VMCNT(20); break;  case 11: GS_VMCNT(22); break;
+    case 12: GS_VMCNT(24); break;  case 13: GS_VMCNT(26); break;
+    case 14: GS_VMCNT(28); break;  default: GS_VMCNT(30); break;
+  }
+}
+#undef GS_VMCNT
+
+// Position in a workgroup's stream of stages.
+struct Cursor {
+  int v;       // work item (unit * heads + head)
+  bool valid;  // false past the workgroup's last item
+  int row0, L, q0, qn, h;
+  int s;       // stage index inside the item
+  int nq, ns;  // query stages, all stages
+};
+
+__device__ __forceinline__ void cursor_load(Cursor& c, const int4* __restrict__ table, int items,
+                                            int heads) {
+  c.valid = c.v < items;
+  c.s = 0;
+  if (c.valid) {
+    const int u = c.v / heads;
+    const int4 e = table[1 + u];  // wave-uniform address: scalar load
+    c.h = c.v - u * heads;
+    c.row0 = e.x; c.L = e.y; c.q0 = e.z; c.qn = e.w;
+    c.nq = (c.qn + ATT_QS - 1) / ATT_QS;
+    c.ns = c.nq + (c.L + ATT_KC - 1) / ATT_KC;
+  }
+}
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const int4* __restrict__ table, int items,
+                                            int heads) {
+  if (++c.s == c.ns) {
+    c.v += gridDim.x;
+    cursor_load(c, table, items, heads);
+  }
 }
 
 __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
-    const bf16* __restrict__ qkv, const int* __restrict__ cu, int S, int B, int d,
+    const bf16* __restrict__ qkv, const int4* __restrict__ table, int heads, int d,
     float scale_log2, bf16* __restrict__ O) {
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][ATT_KC * DH];
-  __shared__ __attribute__((aligned(1024))) bf16 Vt[2][DH * ATT_KC];
+  __shared__ __attribute__((aligned(1024))) bf16 ring[ATT_NST * STAGE_ELEMS];
 
-  AttnUnit U;
-  if (!find_unit<ATT_QG>(cu, S, B, blockIdx.x, U)) return;  // uniform over the workgroup
-  const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ld = 3 * d;
-  const bf16* Qg = qkv + h * DH;
-  const bf16* Kg = qkv + d + h * DH;
-  const bf16* Vg = qkv + 2 * d + h * DH;
-  const int L = U.L;
-  const int nchunks = (L + ATT_KC - 1) / ATT_KC;
+  const int g4 = lane >> 4;   // lane group
+  const int l16 = lane & 15;
+  const int items = table[0].x * heads;
 
-  // --- chunk staging -------------------------------------------------------
-  // K: 64 rows x 16 chunks = 1024 copies of 16 B; one wave instruction fills
-  // 4 key rows (1 KB); 16 instructions, 2 per wave.
-  auto stage_k = [&](int c, int buf) {
+  // Vector-memory ops this wave has issued, and that count right after the
+  // copies of stream positions p .. p+NST-2 (a shift register, no indexing).
+  int ops = 0;
+  int mark[ATT_NST - 1];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int k0 = (j * ATT_WAVES + wave) * 4;   // first key row of this instruction
-      const int kr = k0 + (lane >> 4);
-      const int pc = lane & 15;                     // physical chunk
-      const int lc = pc ^ fk(kr);                   // logical chunk stored there
-      int key = c * ATT_KC + kr;
-      key = key < L ? key : L - 1;
-      const bf16* g = Kg + (size_t)(U.row0 + key) * ld + lc * 8;
-      copy16_to_lds(g, (GS_LDS bf16*)&Ks[buf][k0 * DH]);
-    }
-  };
-  // V: thread -> 4 keys (kg*4..+3) x 4 dh (dg*4..+3); 8-byte loads, then four
-  // 8-byte LDS writes of the transposed 4x4 block.
-  const int vkg = threadIdx.x >> 5;   // 0..15
-  const int vdg = threadIdx.x & 31;   // 0..31
-  auto load_v = [&](int c, uint2* r) {
+  for (int i = 0; i < ATT_NST - 1; ++i) mark[i] = 0;
+
+  // ---- copies of one stage into ring slot `slot` --------------------------
+  // 16 KB = 16 wave copies of 1 KB (4 rows of 256 B); wave w does copies w and
+  // w+8; lane -> row r0 + lane/16, physical chunk lane%16.
+  auto issue = [&](const Cursor& c, int slot) __attribute__((always_inline)) {
+    GS_LDS bf16* dst = (GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
+    const int pc = lane & 15;
+    if (c.s < c.nq) {  // query stage: 64 rows
+      const int q0 = c.q0 + c.s * ATT_QS;
+      const int qlast = c.q0 + c.qn - 1;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      int key = c * ATT_KC + vkg * 4 + kk;
-      key = key < L ? key : L - 1;
-      r[kk] = *(const uint2*)(Vg + (size_t)(U.row0 + key) * ld + vdg * 4);
-    }
-  };
-  auto store_vt = [&](const uint2* r, int buf) {
-    // r[kk] holds dh (vdg*4 + 0..3) of key vkg*4+kk as 4 packed bf16
+      for (int j = 0; j < COPIES; ++j) {
+        const int r0 = (j * ATT_WAVES + wave) * 4;
+        const int rr = r0 + (lane >> 4);
+        int q = q0 + rr;
+        q = q <= qlast ? q : qlast;
+        const int lc = pc ^ swz_q(rr);
+        copy16_to_lds(qkv + (size_t)(c.row0 + q) * ld + c.h * DH + lc * 8, dst + r0 * DH);
+      }
+    } else {           // key chunk: 32 K rows (copy 0) then 32 V rows (copy 1)
+      const int k0 = (c.s - c.nq) * ATT_KC;
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
-      const int e = vdg * 4 + dd;
-      uint32_t lo, hi;  // keys 0,1 and 2,3 of this dh
-      const int sh = (dd & 1) * 16;
-      const uint32_t w0 = (dd < 2) ? r[0].x : r[0].y;
-      const uint32_t w1 = (dd < 2) ? r[1].x : r[1].y;
-      const uint32_t w2 = (dd < 2) ? r[2].x : r[2].y;
-      const uint32_t w3 = (dd < 2) ? r[3].x : r[3].y;
-      lo = ((w0 >> sh) & 0xFFFFu) | (((w1 >> sh) & 0xFFFFu) << 16);
-      hi = ((w2 >> sh) & 0xFFFFu) | (((w3 >> sh) & 0xFFFFu) << 16);
-      const int lchunk = vkg >> 1;                  // 8 keys per 16-byte chunk
-      const int pchunk = lchunk ^ fv(e);
-      GS_LDS u32x2* dst = (GS_LDS u32x2*)((GS_LDS bf16*)&Vt[buf][0] + e * ATT_KC + pchunk * 8 +
-                                          (vkg & 1) * 4);
-      *dst = u32x2{lo, hi};
+      for (int j = 0; j < COPIES; ++j) {
+        const bool isv = j == 1;
+        const int r0 = (j * ATT_WAVES + wave) * 4;
+        const int kr = (r0 + (lane >> 4)) & (ATT_KC - 1);
+        int key = k0 + kr;
+        key = key < c.L ? key : c.L - 1;
+        const int lc = pc ^ (isv ? swz_v(kr) : swz_k(kr));
+        copy16_to_lds(qkv + (size_t)(c.row0 + key) * ld + (isv ? 2 * d : d) + c.h * DH + lc * 8,
+                      dst + r0 * DH);
+      }
     }
+    ops += COPIES;
   };
 
-  // --- queries of this wave -------------------------------------------------
-  // tile t = wave + 8*tt covers block-relative rows q0 + 16t .. +15
-  const int ntiles = (U.qn + 15) >> 4;
-  bool tvalid[2];
-  bf16x8 qf[2][4];
+  // ---- stream -------------------------------------------------------------------
+  Cursor comp, iss;
+  comp.v = blockIdx.x;
+  cursor_load(comp, table, items, heads);
+  if (!comp.valid) return;  // uniform over the workgroup
+  iss = comp;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = wave + ATT_WAVES * tt;
-    tvalid[tt] = t < ntiles;
-    int q = U.q0 + t * 16 + (lane & 15);
-    q = q < L ? q : L - 1;
-    const bf16* qp = Qg + (size_t)(U.row0 + q) * ld + (lane >> 4) * 8;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) qf[tt][kc] = *(const bf16x8*)(qp + kc * 32);
+  for (int s = 0; s < ATT_NST - 1; ++s) {
+    if (iss.valid) {
+      issue(iss, s);
+      cursor_next(iss, table, items, heads);
+    }
+    mark[s] = ops;
   }
 
+  // per-wave query state: rows 32*wave + 16*tt + lane%16 of the current item
+  bf16x8 qf[2][4];
   f32x4 oacc[2][8];
   float mrun[2], lrun[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    mrun[tt] = -INFINITY;
-    lrun[tt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  bool tval[2] = {false, false};
 
-  // prologue: chunk 0
-  {
-    uint2 vr[4];
-    stage_k(0, 0);
-    load_v(0, vr);
-    store_vt(vr, 0);
-  }
-  wait_vmem();
-  __syncthreads();
-
-  const int g4 = lane >> 4;       // lane group: keys g4*8.. of each 32-key pair
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    uint2 vr[4];
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      stage_k(c + 1, buf ^ 1);
-      load_v(c + 1, vr);
+  for (int p = 0; comp.valid; ++p) {
+    const int slot = p & (ATT_NST - 1);
+    // this stage's copies (and everything before them) have landed
+    wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - mark[0]));
+    stream_barrier();             // everyone's landed; everyone is done with stage p-1
+    if (iss.valid) {
+      issue(iss, (p + ATT_NST - 1) & (ATT_NST - 1));  // refill the slot freed by stage p-1
+      cursor_next(iss, table, items, heads);
     }
-    const GS_LDS bf16* ks = (const GS_LDS bf16*)&Ks[buf][0];
-    const GS_LDS bf16* vt = (const GS_LDS bf16*)&Vt[buf][0];
+#pragma unroll
+    for (int i = 0; i < ATT_NST - 2; ++i) mark[i] = mark[i + 1];
+    mark[ATT_NST - 2] = ops;  // position p+NST-1 (if issued; otherwise never waited for)
+    const GS_LDS bf16* st = (const GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
 
-    // S^T tiles for both query tiles: s[tt][ks] holds keys
-    //   c*64 + (ks/2)*32 + g4*8 + (ks&1)*4 + i,  i = 0..3, for query lane&15
-    f32x4 s[2][4];
+    if (comp.s < comp.nq) {
+      // ---- query stage: the waves owning these 128 rows load their tiles ----
+      const int wfirst = comp.s * (ATT_QS / 32);  // 2 waves per query stage
+      if (comp.s == 0) tval[0] = tval[1] = false;
+      if (wave >= wfirst && wave < wfirst + ATT_QS / 32) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int kr = perm_key(kt, lane & 15);
-      bf16x8 kf[4];
+        for (int tt = 0; tt < 2; ++tt) {
+          const int rr = (wave - wfirst) * 32 + tt * 16 + l16;
+          tval[tt] = (wave * 32 + tt * 16) < comp.qn;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int lc = kc * 4 + g4;
-        kf[kc] = *(const GS_LDS bf16x8*)(ks + kr * DH + (lc ^ fk(kr)) * 8);
+          for (int kc = 0; kc < 4; ++kc) {
+            const int lc = kc * 4 + g4;
+            qf[tt][kc] = *(const GS_LDS bf16x8*)(st + rr * DH + (lc ^ swz_q(rr)) * 8);
+          }
+          mrun[tt] = -INFINITY;
+          lrun[tt] = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
+    } else if (tval[0]) {
+      // ---- key chunk (32 keys) ----
+      const int c = comp.s - comp.nq;
+      const int kvalid = min(ATT_KC, comp.L - c * ATT_KC);  // keys of this chunk in the block
+      const GS_LDS bf16* ks = st;
+      const GS_LDS bf16* vs = st + ATT_KC * DH;
+
+      // S^T for the two 16-key tiles; tile kt row r feeds key perm_key(kt, r)
+      f32x4 s[2][2];
+      bf16x8 kf[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int kr = perm_key(kt, l16);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          kf[kt][kc] = *(const GS_LDS bf16x8*)(ks + kr * DH + ((kc * 4 + g4) ^ swz_k(kr)) * 8);
+      }
+      // tile 1 holds keys {4..7, 12..15, 20..23, 28..31}: it has a valid key iff kvalid > 4
+      const bool two = kvalid > 4;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[0][kt] = s[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kt == 0 || two) {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+            s[0][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][kc], qf[0][kc], s[0][kt], 0, 0, 0);
+          if (tval[1]) {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+              s[1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][kc], qf[1][kc], s[1][kt], 0, 0, 0);
+          }
+        }
+      }
+
+      // online softmax; P in the PV operand layout (lane holds keys g4*8 + j)
+      bf16x8 pf[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        float mx = -INFINITY;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc], qf[tt][kc], a, 0, 0, 0);
-        s[tt][kt] = a;
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = g4 * 8 + kt * 4 + i;
+            const float v = key < kvalid ? s[tt][kt][i] * scale_log2 : -INFINITY;
+            s[tt][kt][i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mrun[tt], mx);
+        const float alpha = exp2f(mrun[tt] - mnew);
+        mrun[tt] = mnew;
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16 pb = to_bf16(exp2f(s[tt][kt][i] - mnew));
+            psum += to_f32(pb);
+            pf[tt][kt * 4 + i] = pb;
+          }
+        lrun[tt] = lrun[tt] * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= alpha;
       }
-    }
 
-    // online softmax (base 2) and P in the PV operand layout
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = c * ATT_KC + (kt >> 1) * 32 + g4 * 8 + (kt & 1) * 4 + i;
-          float v = s[tt][kt][i] * scale_log2;
-          v = key < L ? v : -INFINITY;
-          s[tt][kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[tt], mx);
-      const float alpha = exp2f(mrun[tt] - mnew);
-      mrun[tt] = mnew;
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16 pb = to_bf16(exp2f(s[tt][kt][i] - mnew));
-          psum += to_f32(pb);
-          pf[tt][kt >> 1][(kt & 1) * 4 + i] = pb;
-        }
-      lrun[tt] = lrun[tt] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= alpha;
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
+      // O^T += V^T P^T.  The V^T fragment (16 dh x 32 keys) is two transposing
+      // reads: this lane addresses V row g4*8 + r*4 + l16/4 at dh
+      // dt*16 + 4*(l16%4).
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int e = dt * 16 + (lane & 15);
-        const int lc = pr * 4 + g4;
-        const bf16x8 vf = *(const GS_LDS bf16x8*)(vt + e * ATT_KC + (lc ^ fv(e)) * 8);
+        const GS_LDS bf16* va[2];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          oacc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[tt][pr], oacc[tt][dt], 0, 0, 0);
+        for (int r = 0; r < 2; ++r) {
+          const int kr = g4 * 8 + r * 4 + (l16 >> 2);
+          const int e0 = dt * 16 + 4 * (l16 & 3);
+          va[r] = vs + kr * DH + (((e0 >> 3) ^ swz_v(kr)) * 8) + (e0 & 7);
+        }
+        const bf16x8 vf = lds_read_tr_pair(va[0], va[1]);
+        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], oacc[0][dt], 0, 0, 0);
+        if (tval[1])
+          oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], oacc[1][dt], 0, 0, 0);
+      }
+
+      // ---- last chunk of the item: normalise and store ----
+      if (comp.s == comp.ns - 1) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          if (!tval[tt]) continue;
+          float l = lrun[tt];
+          l += __shfl_xor(l, 16);
+          l += __shfl_xor(l, 32);
+          const float inv = 1.f / l;
+          const int q = comp.q0 + wave * 32 + tt * 16 + l16;
+          if (q < comp.q0 + comp.qn) {
+            bf16* op = O + (size_t)(comp.row0 + q) * d + comp.h * DH + g4 * 4;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+              bf16x4 o;
+              o[0] = to_bf16(oacc[tt][dt][0] * inv);
+              o[1] = to_bf16(oacc[tt][dt][1] * inv);
+              o[2] = to_bf16(oacc[tt][dt][2] * inv);
+              o[3] = to_bf16(oacc[tt][dt][3] * inv);
+              *(bf16x4*)(op + dt * 16) = o;
+            }
+          }
+          ops += 8;  // issued by the lanes that store; counted per wave either way
+        }
       }
     }
-
-    if (more) store_vt(vr, buf ^ 1);
-    wait_vmem();
-    __syncthreads();
-  }
-
-  // normalise and store: oacc[tt][dt][i] is O[query lane&15][dh dt*16 + g4*4 + i]
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    if (!tvalid[tt]) continue;
-    float l = lrun[tt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = 1.f / l;
-    const int t = wave + ATT_WAVES * tt;
-    const int q = U.q0 + t * 16 + (lane & 15);
-    if (q >= L) continue;
-    bf16* op = O + (size_t)(U.row0 + q) * d + h * DH + g4 * 4;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      bf16x4 o;
-      o[0] = to_bf16(oacc[tt][dt][0] * inv);
-      o[1] = to_bf16(oacc[tt][dt][1] * inv);
-      o[2] = to_bf16(oacc[tt][dt][2] * inv);
-      o[3] = to_bf16(oacc[tt][dt][3] * inv);
-      *(bf16x4*)(op + dt * 16) = o;
-    }
+    cursor_next(comp, table, items, heads);
   }
 }
 
+static int g_num_cus = 0;
+
+int attn_bf16_table_entries(long long N) { return (int)(N + 1); }
+
 hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long long N, int d,
-                                  int heads, int B, void* o, hipStream_t stream) {
-  const int units = attn_unit_bound(N, S, B, ATT_QG);
+                                  int heads, int B, void* o, void* table, hipStream_t stream) {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_num_cus = n;
+  }
+  hipLaunchKernelGGL(build_unit_table_kernel<ATT_QG>, dim3(1), dim3(1024), 0, stream, cu, S, B,
+                     (int4*)table);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long items = (long long)attn_unit_bound(N, S, B, ATT_QG) * heads;
+  const int grid = items < g_num_cus ? (int)items : g_num_cus;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-  hipLaunchKernelGGL(block_attn_bf16_kernel, dim3(units, heads), dim3(ATT_THREADS), 0, stream,
-                     (const bf16*)qkv, cu, S, B, d, scale_log2, (bf16*)o);
+  hipLaunchKernelGGL(block_attn_bf16_kernel, dim3(grid), dim3(ATT_THREADS), 0, stream,
+                     (const bf16*)qkv, (const int4*)table, heads, d, scale_log2, (bf16*)o);
   return hipGetLastError();
 }
 

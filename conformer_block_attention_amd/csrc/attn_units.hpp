@@ -69,6 +69,48 @@ __device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnU
   return false;
 }
 
+// Unit table for kernels that read their units with scalar loads.
+// table[0].x = number of units; table[1 + u] = {row0, L, q0, qn} of unit u.
+// Every unit holds at least one row, so N + 1 entries always suffice.
+// One workgroup; sequences are scanned 1024 at a time (block-wide prefix sum).
+template <int QG>
+__global__ __launch_bounds__(1024) void build_unit_table_kernel(const int* __restrict__ cu, int S,
+                                                               int B, int4* __restrict__ table) {
+  __shared__ int scan[1024];
+  const int tid = threadIdx.x;
+  const int upb = (B - 1) / QG + 1;
+  int base = 0;
+  for (int c0 = 0; c0 < S; c0 += 1024) {
+    const int s = c0 + tid;
+    int len = 0;
+    if (s < S) len = cu[s + 1] - cu[s];
+    const int n = units_of_seq<QG>(len, B, upb);
+    scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+      const int y = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += y;
+      __syncthreads();
+    }
+    const int excl = base + scan[tid] - n;
+    if (n > 0) {
+      const int start = cu[s];
+      const int nb = (len - 1) / B + 1;
+      for (int v = 0; v < n; ++v) {
+        int j = v / upb;
+        if (j > nb - 1) j = nb - 1;
+        const int g = v - j * upb;
+        const int L = (j < nb - 1) ? B : len - (nb - 1) * B;
+        table[1 + excl + v] = make_int4(start + j * B, L, g * QG, min(QG, L - g * QG));
+      }
+    }
+    base += scan[1023];
+    __syncthreads();
+  }
+  if (tid == 0) table[0] = make_int4(base, 0, 0, 0);
+}
+
 // Upper bound on the number of units of N rows in S sequences:
 // sum_s ceil(len_s/B) <= N/B + S, plus N/QG more query groups when B > QG.
 inline int attn_unit_bound(long long N, int S, int B, int QG) {

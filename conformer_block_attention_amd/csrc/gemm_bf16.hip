@@ -30,43 +30,73 @@
 namespace gs {
 
 constexpr int GEMM_BM = 256;
-constexpr int GEMM_BK = 64;
 constexpr int GEMM_THREADS = 256;
 
-// Issue the 16-byte LDS-direct copies of one [ROWS x 64] bf16 tile.
-// Each wave instruction fills 8 consecutive LDS rows (1 KB).
-template <int ROWS>
+// LDS tile geometry for a K step of BK bf16: a row is BK*2 bytes = BK/8
+// chunks of 16 bytes.  gfx950 serves a 16-byte-per-lane LDS read 16 lanes at
+// a time from a 256-byte window of banks; the fragment reads below touch 16
+// consecutive rows at one logical chunk, so the physical chunk of row r is the
+// logical one XOR-ed with (r / rows_per_window) mod chunks_per_row: the 16
+// rows then land on 16 distinct 16-byte bank slots.
+template <int BK>
+struct TileGeom {
+  static constexpr int CPR = BK / 8;                 // 16-byte chunks per row
+  static constexpr int RPW = 256 / (BK * 2);         // rows per 256-byte bank window
+  static constexpr int ROWS_PER_COPY = 1024 / (BK * 2);  // rows one wave copy fills
+  __device__ static __forceinline__ int swz(int r) { return (r / RPW) % CPR; }
+};
+
+// Issue the 16-byte LDS-direct copies of one [ROWS x BK] bf16 tile (ROWS rows
+// starting at global row row0, k columns k0..k0+BK-1).  Each wave instruction
+// fills ROWS_PER_COPY consecutive LDS rows (1 KB); rows past row_limit are
+// clamped (their results are never stored).
+template <int ROWS, int BK>
 __device__ __forceinline__ void stage_tile(const bf16* __restrict__ src, int row0, int row_limit,
                                            int ld, int k0, GS_LDS bf16* dst, int wave, int lane) {
-  constexpr int INSTR = ROWS / 8 / 4;  // per wave
+  using G = TileGeom<BK>;
+  constexpr int INSTR = ROWS / G::ROWS_PER_COPY / 4;  // per wave
 #pragma unroll
   for (int j = 0; j < INSTR; ++j) {
-    const int r0 = (j * 4 + wave) * 8;        // first LDS row of this instruction
-    const int r = r0 + (lane >> 3);           // LDS row this lane fills
-    const int p = lane & 7;                   // physical 16-byte chunk in the row
-    const int c = p ^ (r & 7);                // logical chunk stored there
+    const int r0 = (j * 4 + wave) * G::ROWS_PER_COPY;  // first LDS row of this copy
+    const int r = r0 + lane / G::CPR;                  // LDS row this lane fills
+    const int p = lane % G::CPR;                       // physical chunk in the row
+    const int c = p ^ G::swz(r);                       // logical chunk stored there
     int gr = row0 + r;
-    gr = gr < row_limit ? gr : row_limit - 1;  // clamp rows past the end
-    const bf16* g = src + (size_t)gr * ld + k0 + c * 8;
-    copy16_to_lds(g, dst + r0 * GEMM_BK);
+    gr = gr < row_limit ? gr : row_limit - 1;
+    copy16_to_lds(src + (size_t)gr * ld + k0 + c * 8, dst + r0 * BK);
   }
 }
 
-template <int BN, bool RESID>
+// vmcnt(N) with lgkmcnt/expcnt at max (gfx9 s_waitcnt encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// C[M][Nc] = (R +) A[M][K] . W[Nc][K]^T.  Tile 256 x BN, K step BK, NST-stage
+// LDS ring (copies for K steps kt+1..kt+NST-1 are in flight while kt is multiplied).
+template <int BN, int BK, int NST, bool RESID>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* R, bf16* C,
     int M, int Nc, int K) {
+  using G = TileGeom<BK>;
   constexpr int WN = BN / 2;   // wave tile columns
   constexpr int TI = 4;        // 32-row MFMA tiles per wave (128 rows)
   constexpr int TJ = WN / 32;  // 32-col MFMA tiles per wave
-  __shared__ __attribute__((aligned(1024))) bf16 As[2][GEMM_BM * GEMM_BK];
-  __shared__ __attribute__((aligned(1024))) bf16 Bs[2][BN * GEMM_BK];
+  constexpr int KK = BK / 16;  // MFMA k chunks per K step
+  constexpr int A_ELEMS = GEMM_BM * BK, B_ELEMS = BN * BK;
+  // copies per stage per wave (the vmcnt unit)
+  constexpr int LPS = GEMM_BM / G::ROWS_PER_COPY / 4 + BN / G::ROWS_PER_COPY / 4;
+  static_assert(KK % 2 == 0, "register double buffer assumes an even chunk count");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NST * (A_ELEMS + B_ELEMS)];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // tile id remap: contiguous ranges of tiles per XCD
+  // tile id remap: the 8 XCDs receive workgroup ids round-robin; give each
+  // XCD a contiguous range of tiles (column tiles of a row panel share its L2)
   const int mt_count = (M + GEMM_BM - 1) / GEMM_BM;
   const int nt_count = Nc / BN + (Nc % BN ? 1 : 0);
   const int T = mt_count * nt_count;
@@ -76,6 +106,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   const int m0 = (t / nt_count) * GEMM_BM;
   const int n0 = (t % nt_count) * BN;
 
+  auto sA = [&](int st) { return (GS_LDS bf16*)&smem[st * (A_ELEMS + B_ELEMS)]; };
+  auto sB = [&](int st) { return (GS_LDS bf16*)&smem[st * (A_ELEMS + B_ELEMS) + A_ELEMS]; };
+  auto issue = [&](int kt) {
+    const int st = kt % NST;
+    stage_tile<GEMM_BM, BK>(A, m0, M, K, kt * BK, sA(st), wave, lane);
+    stage_tile<BN, BK>(W, n0, Nc, K, kt * BK, sB(st), wave, lane);
+  };
+
   f32x16 acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
@@ -84,58 +122,57 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int KT = K / GEMM_BK;
-  GS_LDS bf16* as0 = (GS_LDS bf16*)&As[0][0];
-  GS_LDS bf16* as1 = (GS_LDS bf16*)&As[1][0];
-  GS_LDS bf16* bs0 = (GS_LDS bf16*)&Bs[0][0];
-  GS_LDS bf16* bs1 = (GS_LDS bf16*)&Bs[1][0];
-
-  // fragment read offsets (in bf16 elements) inside a stage
+  const int KT = K / BK;
   const int frag_row = lane & 31;
   const int half = lane >> 5;
 
-  // fragments of one 16-wide k chunk: A rows (activations) and W rows (weights)
-  auto load_frags = [&](const GS_LDS bf16* as, const GS_LDS bf16* bs, int kk, bf16x8* af,
-                        bf16x8* bfr) {
-    const int phys = ((kk * 2 + half) ^ (frag_row & 7)) * 8;
+  // fragments of one 16-wide k chunk (A rows = activations, W rows = weights)
+  auto load_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr) {
+    const GS_LDS bf16* as = sA(st);
+    const GS_LDS bf16* bs = sB(st);
+    const int c = kk * 2 + half;
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-      af[i] = *(const GS_LDS bf16x8*)(as + (wm * 128 + i * 32 + frag_row) * GEMM_BK + phys);
+    for (int i = 0; i < TI; ++i) {
+      const int r = wm * 128 + i * 32 + frag_row;
+      af[i] = *(const GS_LDS bf16x8*)(as + r * BK + (c ^ G::swz(r)) * 8);
+    }
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      bfr[j] = *(const GS_LDS bf16x8*)(bs + (wn * WN + j * 32 + frag_row) * GEMM_BK + phys);
+    for (int j = 0; j < TJ; ++j) {
+      const int r = wn * WN + j * 32 + frag_row;
+      bfr[j] = *(const GS_LDS bf16x8*)(bs + r * BK + (c ^ G::swz(r)) * 8);
+    }
   };
 
-  stage_tile<GEMM_BM>(A, m0, M, K, 0, as0, wave, lane);
-  stage_tile<BN>(W, n0, Nc, K, 0, bs0, wave, lane);
-  wait_vmem();
+  // prologue: fill all NST stages (K steps 0..NST-1), wait for step 0.
+  // Invariant in the loop: while step kt is multiplied, steps kt+1..kt+NST-1
+  // are in flight; after step kt's last reads, its stage is refilled with
+  // step kt+NST.
+#pragma unroll
+  for (int s = 0; s < NST; ++s)
+    if (s < KT) issue(s);
+  if (KT >= NST) wait_vmcnt<LPS * (NST - 1)>(); else wait_vmem();
   __syncthreads();
 
-  // Software pipeline.  Registers hold two k chunks: while the 16 MFMAs of
-  // chunk kk run, the LDS reads of chunk kk+1 are in flight.  The stage
-  // barrier sits in the last chunk, so the first chunk of the next stage is
-  // read while the last chunk of this one is multiplied.
+  // Registers hold two k chunks: while chunk kk's MFMAs run, chunk kk+1's LDS
+  // reads are in flight.  The stage barrier sits before the last chunk's
+  // MFMAs, so the next step's first chunk is read under them, and the freed
+  // stage is refilled right after the barrier.
   bf16x8 af[2][TI], bfr[2][TJ];
-  load_frags(as0, bs0, 0, af[0], bfr[0]);
-  constexpr int KK = GEMM_BK / 16;
+  load_frags(0, 0, af[0], bfr[0]);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) {
-      stage_tile<GEMM_BM>(A, m0, M, K, (kt + 1) * GEMM_BK, cur ? as0 : as1, wave, lane);
-      stage_tile<BN>(W, n0, Nc, K, (kt + 1) * GEMM_BK, cur ? bs0 : bs1, wave, lane);
-    }
-    const GS_LDS bf16* as = cur ? as1 : as0;
-    const GS_LDS bf16* bs = cur ? bs1 : bs0;
+    const int st = kt % NST;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int p = kk & 1;  // KK is even: chunk parity is the same in every stage
-      wait_lds();            // chunk kk is in registers
+      const int p = kk & 1;
+      wait_lds();  // chunk kk is in registers; all reads of this stage so far are done
       if (kk + 1 < KK) {
-        load_frags(as, bs, kk + 1, af[p ^ 1], bfr[p ^ 1]);
-      } else {
-        wait_vmem();         // next stage landed (this wave's copies) ...
-        __syncthreads();     // ... and everyone's; everyone is done with this stage
-        if (kt + 1 < KT) load_frags(cur ? as0 : as1, cur ? bs0 : bs1, 0, af[p ^ 1], bfr[p ^ 1]);
+        load_frags(st, kk + 1, af[p ^ 1], bfr[p ^ 1]);
+      } else if (kt + 1 < KT) {
+        // step kt+1 must have landed: after its copies only steps kt+2..kt+NST-1 may be pending
+        if (kt + NST - 1 < KT) wait_vmcnt<LPS * (NST - 2)>(); else wait_vmem();
+        __syncthreads();                    // all waves are done reading stage st
+        if (kt + NST < KT) issue(kt + NST);  // refill the freed stage
+        load_frags((kt + 1) % NST, 0, af[p ^ 1], bfr[p ^ 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -183,7 +220,7 @@ static inline int gemm_grid(int M, int Nc, int BN) {
 hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int M, int d,
                                 hipStream_t stream) {
   const int Nc = 3 * d;
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<256, false>), dim3(gemm_grid(M, Nc, 256)),
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<256, 64, 2, false>), dim3(gemm_grid(M, Nc, 256)),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)x, (const bf16*)wqkv,
                      (const bf16*)nullptr, (bf16*)qkv, M, Nc, d);
   return hipGetLastError();
@@ -191,7 +228,7 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int 
 
 hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
                                 int d, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<128, true>), dim3(gemm_grid(M, d, 128)),
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<128, 64, 2, true>), dim3(gemm_grid(M, d, 128)),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)o, (const bf16*)wo,
                      (const bf16*)x, (bf16*)out, M, d, d);
   return hipGetLastError();

@@ -20,7 +20,7 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int 
 hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
                                 int d, hipStream_t stream);
 hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long long N, int d,
-                                  int heads, int B, void* o, hipStream_t stream);
+                                  int heads, int B, void* o, void* table, hipStream_t stream);
 hipError_t launch_qkv_proj_f32(const void* x, const void* wqkv, void* qkv, int M, int d,
                                hipStream_t stream);
 hipError_t launch_out_proj_f32(const void* o, const void* wo, const void* x, void* out, int M,
@@ -151,12 +151,19 @@ const char* gs_status_string(gs_status s) {
 
 const char* gs_last_error_detail(void) { return g_detail; }
 
+size_t gs_block_attn_workspace_bytes(int64_t total_frames) {
+  if (total_frames < 0) return 0;
+  // work-unit table: a count and at most one 16-byte entry per row
+  return align_up(16 * ((size_t)total_frames + 1));
+}
+
 size_t gs_block_mhsa_workspace_bytes(int64_t total_frames, int32_t d_model, gs_dtype dtype) {
   if (total_frames < 0 || d_model < 1 || (dtype != GS_F32 && dtype != GS_BF16)) return 0;
   const size_t e = elem_size(dtype);
   const size_t n = (size_t)total_frames, d = (size_t)d_model;
-  // Q|K|V [N][3d], O [N][d], one aligned slot for the debug flag
-  return align_up(n * 3 * d * e) + align_up(n * d * e) + kAlign;
+  // Q|K|V [N][3d], O [N][d], the attention step's unit table, a debug flag slot
+  return align_up(n * 3 * d * e) + align_up(n * d * e) + gs_block_attn_workspace_bytes(total_frames) +
+         kAlign;
 }
 
 gs_status gs_qkv_proj(const void* x, const void* Wqkv, void* qkv, int64_t total_frames,
@@ -175,7 +182,8 @@ gs_status gs_qkv_proj(const void* x, const void* Wqkv, void* qkv, int64_t total_
 
 gs_status gs_block_attn(const void* qkv, const int32_t* cu_seqlens, int32_t num_seqs,
                         int64_t total_frames, int32_t d_model, int32_t heads,
-                        int32_t block_frames, gs_dtype dtype, void* o, hipStream_t stream) {
+                        int32_t block_frames, gs_dtype dtype, void* o, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
   GS_TRY(check_dtype(dtype));
   GS_TRY(check_dims(total_frames, d_model));
   GS_TRY(check_heads(d_model, heads));
@@ -185,10 +193,17 @@ gs_status gs_block_attn(const void* qkv, const int32_t* cu_seqlens, int32_t num_
   if (total_frames == 0) return GS_OK;
   GS_TRY(check_ptr(qkv, "qkv"));
   GS_TRY(check_ptr(o, "o"));
+  if (!workspace) return fail(GS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  const size_t need = gs_block_attn_workspace_bytes(total_frames);
+  if (workspace_bytes < need)
+    return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   const long long N = total_frames;
   hipError_t e =
       dtype == GS_BF16
-          ? gs::launch_block_attn_bf16(qkv, cu_seqlens, num_seqs, N, d_model, heads, block_frames, o, stream)
+          ? gs::launch_block_attn_bf16(qkv, cu_seqlens, num_seqs, N, d_model, heads, block_frames, o,
+                                       workspace, stream)
           : gs::launch_block_attn_f32(qkv, cu_seqlens, num_seqs, N, d_model, heads, block_frames, o, stream);
   return hip_status(e, "block_attn launch");
 }
@@ -245,14 +260,16 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
   char* ws = (char*)desc->workspace;
   void* qkv = ws;
   void* o = ws + align_up((size_t)N * 3 * d * e);
-  int* dflag = (int*)(ws + align_up((size_t)N * 3 * d * e) + align_up((size_t)N * d * e));
+  char* table = (char*)o + align_up((size_t)N * d * e);
+  const size_t table_bytes = gs_block_attn_workspace_bytes(N);
+  int* dflag = (int*)(table + table_bytes);
   GS_TRY(debug_check_cu(cu_seqlens, desc->num_seqs, N, dflag, stream));
 
   GS_TRY(record(desc, 0, stream));
   GS_TRY(gs_qkv_proj(x, Wqkv, qkv, N, d, desc->dtype, stream));
   GS_TRY(record(desc, 1, stream));
   GS_TRY(gs_block_attn(qkv, cu_seqlens, desc->num_seqs, N, d, heads, block_frames, desc->dtype, o,
-                       stream));
+                       table, table_bytes, stream));
   GS_TRY(record(desc, 2, stream));
   GS_TRY(gs_out_proj_residual(o, Wo, x, out, N, d, desc->dtype, stream));
   GS_TRY(record(desc, 3, stream));

@@ -21,7 +21,8 @@ GS_F32, GS_BF16 = 0, 1
 
 EXPORTS = (
     "gs_block_mhsa_workspace_bytes", "gs_block_mhsa_fwd", "gs_qkv_proj", "gs_block_attn",
-    "gs_out_proj_residual", "gs_status_string", "gs_last_error_detail", "gs_version",
+    "gs_block_attn_workspace_bytes", "gs_out_proj_residual", "gs_status_string",
+    "gs_last_error_detail", "gs_version",
 )
 
 
@@ -65,7 +66,9 @@ def load(path: Optional[str] = None):
     lib.gs_qkv_proj.restype = ctypes.c_int
     lib.gs_qkv_proj.argtypes = [P, P, P, I64, I32, ctypes.c_int, P]
     lib.gs_block_attn.restype = ctypes.c_int
-    lib.gs_block_attn.argtypes = [P, P, I32, I64, I32, I32, I32, ctypes.c_int, P, P]
+    lib.gs_block_attn.argtypes = [P, P, I32, I64, I32, I32, I32, ctypes.c_int, P, P, ctypes.c_size_t, P]
+    lib.gs_block_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_block_attn_workspace_bytes.argtypes = [I64]
     lib.gs_out_proj_residual.restype = ctypes.c_int
     lib.gs_out_proj_residual.argtypes = [P, P, P, P, I64, I32, ctypes.c_int, P]
     lib.gs_status_string.restype = ctypes.c_char_p
@@ -152,17 +155,22 @@ def qkv_proj(x: torch.Tensor, wqkv: torch.Tensor, qkv: Optional[torch.Tensor] = 
 
 
 def block_attn(qkv: torch.Tensor, cu_seqlens: torch.Tensor, heads: int, block_frames: int,
-               o: Optional[torch.Tensor] = None, stream=None):
+               o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None):
+    lib = load()
     n, d3 = qkv.shape
     d = d3 // 3
     if o is None:
         o = torch.empty((n, d), dtype=qkv.dtype, device=qkv.device)
+    if workspace is None:
+        nb = int(lib.gs_block_attn_workspace_bytes(int(n)))
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=qkv.device)
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
-    _check(load().gs_block_attn(_dev(qkv, "qkv"), _dev(cu_seqlens, "cu_seqlens"),
-                                int(cu_seqlens.numel()) - 1, int(n), int(d), int(heads),
-                                int(block_frames), _gs_dtype(qkv.dtype), _dev(o, "o", qkv.dtype),
-                                _stream(stream)))
+    _check(lib.gs_block_attn(_dev(qkv, "qkv"), _dev(cu_seqlens, "cu_seqlens"),
+                             int(cu_seqlens.numel()) - 1, int(n), int(d), int(heads),
+                             int(block_frames), _gs_dtype(qkv.dtype), _dev(o, "o", qkv.dtype),
+                             _dev(workspace, "workspace"), int(workspace.numel()), _stream(stream)))
     return o
 
 

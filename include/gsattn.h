@@ -70,7 +70,9 @@ typedef struct {
   int32_t d_model;         /* d */
   gs_dtype dtype;
   void* workspace;         /* device scratch, >= gs_block_mhsa_workspace_bytes() bytes,
-                              256-byte aligned; holds Q|K|V [N][3d] then O [N][d] */
+                              256-byte aligned; holds Q|K|V [N][3d], O [N][d] and the
+                              attention step's work-unit table; contents on entry are
+                              ignored, contents on return are unspecified */
   size_t workspace_bytes;
   /* Optional (may be NULL): four events the library records on `stream`
      before the projection kernel, after it, after the attention kernel and
@@ -105,13 +107,20 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
 gs_status gs_qkv_proj(const void* x, const void* Wqkv, void* qkv, int64_t total_frames,
                       int32_t d_model, gs_dtype dtype, hipStream_t stream);
 
+/* Bytes of workspace gs_block_attn needs for total_frames rows (0 on bad input). */
+size_t gs_block_attn_workspace_bytes(int64_t total_frames);
+
 /*
  * Step 2 alone: o[N][d] from qkv[N][3d] (layout as produced by gs_qkv_proj):
  * per block and head, softmax(Q K^T / sqrt(dh)) V, keys limited to the block.
+ *   workspace  device scratch of >= gs_block_attn_workspace_bytes(N) bytes,
+ *              256-byte aligned (the table of work units built from cu_seqlens);
+ *              calls that share a workspace must not overlap in time.
  */
 gs_status gs_block_attn(const void* qkv, const int32_t* cu_seqlens, int32_t num_seqs,
                         int64_t total_frames, int32_t d_model, int32_t heads,
-                        int32_t block_frames, gs_dtype dtype, void* o, hipStream_t stream);
+                        int32_t block_frames, gs_dtype dtype, void* o, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Step 3 alone: out[N][d] = x[N][d] + o[N][d] . Wo[d][d]^T (fp32 accumulate and

@@ -42,10 +42,11 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_bytes(lib):
     n, d = 1000, 1024
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert lib.gs_block_attn_workspace_bytes(n) == al(16 * (n + 1))
     for dt, e in ((gsattn.GS_BF16, 2), (gsattn.GS_F32, 4)):
         got = lib.gs_block_mhsa_workspace_bytes(n, d, dt)
-        al = lambda v: (v + 255) // 256 * 256  # noqa: E731
-        assert got == al(n * 3 * d * e) + al(n * d * e) + 256
+        assert got == al(n * 3 * d * e) + al(n * d * e) + al(16 * (n + 1)) + 256
     assert lib.gs_block_mhsa_workspace_bytes(-1, d, gsattn.GS_BF16) == 0
     assert lib.gs_block_mhsa_workspace_bytes(n, d, 7) == 0
 
@@ -97,8 +98,12 @@ def test_empty_input_is_noop(lib):
 def test_stage_argument_errors(lib):
     assert lib.gs_qkv_proj(None, FAKE, FAKE, 10, 1024, gsattn.GS_BF16, None) == gsattn.GS_ERR_INVALID_ARGUMENT
     assert lib.gs_qkv_proj(FAKE, FAKE, FAKE, 10, 96, gsattn.GS_BF16, None) == gsattn.GS_ERR_UNSUPPORTED
-    assert lib.gs_block_attn(FAKE, FAKE, 0, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, None) == gsattn.GS_ERR_INVALID_ARGUMENT
-    assert lib.gs_block_attn(FAKE, None, 1, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, None) == gsattn.GS_ERR_INVALID_ARGUMENT
-    assert lib.gs_block_attn(FAKE, FAKE, 1, 10, 1024, 8, 0, gsattn.GS_BF16, FAKE, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    W, WB = FAKE * 16, 1 << 20
+    assert lib.gs_block_attn(FAKE, FAKE, 0, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, W, WB, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_block_attn(FAKE, None, 1, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, W, WB, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_block_attn(FAKE, FAKE, 1, 10, 1024, 8, 0, gsattn.GS_BF16, FAKE, W, WB, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_block_attn(FAKE, FAKE, 1, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, None, WB, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_block_attn(FAKE, FAKE, 1, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, W + 8, WB, None) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_block_attn(FAKE, FAKE, 1, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, W, 16, None) == gsattn.GS_ERR_WORKSPACE_TOO_SMALL
     assert lib.gs_out_proj_residual(FAKE, FAKE, None, FAKE, 10, 1024, gsattn.GS_F32, None) == gsattn.GS_ERR_INVALID_ARGUMENT
     assert lib.gs_qkv_proj(FAKE, FAKE, FAKE, 1 << 31, 1024, gsattn.GS_BF16, None) == gsattn.GS_ERR_UNSUPPORTED
