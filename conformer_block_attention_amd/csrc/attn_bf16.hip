@@ -66,24 +66,53 @@ __device__ __forceinline__ int perm_key(int kt, int r) {
   return (kt >> 1) * 32 + (r >> 2) * 8 + (kt & 1) * 4 + (r & 3);
 }
 
-// Two transposing LDS reads (ds_read_b64_tr_b16) and a wait for them, in one
-// asm block so both results are complete when it ends.  (Through the builtin,
+// Four transposing LDS reads (ds_read_b64_tr_b16) and a wait for them, in one
+// asm block, so the results are complete when it ends.  (Through the builtin,
 // the compiler makes every such read wait for all in-flight global->LDS
 // copies, which would drain the ring; ordering against those copies is
-// enforced here by the explicit waits and barriers of the stream loop.)
-__device__ __forceinline__ bf16x8 lds_read_tr_pair(const GS_LDS bf16* p0, const GS_LDS bf16* p1) {
-  unsigned long long r0, r1;
-  const unsigned a0 = (unsigned)(uintptr_t)p0, a1 = (unsigned)(uintptr_t)p1;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %2\n\t"
-      "ds_read_b64_tr_b16 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1)
-      : "v"(a0), "v"(a1)
-      : "memory");
+// enforced by the explicit waits and barriers of the stream loop.)
+__device__ __forceinline__ void lds_read_tr_x4(const GS_LDS bf16* const* p, bf16x8* out) {
   typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(bf16x8, u64x2{r0, r1});
+  unsigned long long r[4];
+  unsigned a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = (unsigned)(uintptr_t)p[i];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+  out[0] = __builtin_bit_cast(bf16x8, u64x2{r[0], r[1]});
+  out[1] = __builtin_bit_cast(bf16x8, u64x2{r[2], r[3]});
 }
+
+// Max / sum of a value over the lane pairs (l, l^32) and (l, l^16), with the
+// gfx950 cross-lane swaps (VALU, no LDS round trip).  Each swap leaves, in
+// every lane, the lane's own value and its partner's in the two results.
+__device__ __forceinline__ float xmax_lanes32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax_lanes16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum_lanes32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum_lanes16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The softmax reference max moves only when a row max exceeds it by more than
+// this many doublings (P stays <= 2^8, well inside bf16 and fp32 range).
+constexpr float LAZY_RESCALE = 8.f;
 
 // Workgroup barrier without a memory fence.  A fence would make every wave
 // wait for all of its outstanding global->LDS copies and global stores; the
@@ -201,13 +230,16 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   };
 
   // ---- stream -------------------------------------------------------------------
+  // Copies run AHEAD = NST-2 stages ahead: the slot of the previous stage stays
+  // resident for one more iteration, because its PV product is done then.
+  constexpr int AHEAD = ATT_NST - 2;
   Cursor comp, iss;
   comp.v = blockIdx.x;
   cursor_load(comp, table, items, heads);
   if (!comp.valid) return;  // uniform over the workgroup
   iss = comp;
 #pragma unroll
-  for (int s = 0; s < ATT_NST - 1; ++s) {
+  for (int s = 0; s < AHEAD; ++s) {
     if (iss.valid) {
       issue(iss, s);
       cursor_next(iss, table, items, heads);
@@ -218,25 +250,125 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   // per-wave query state: rows 32*wave + 16*tt + lane%16 of the current item
   bf16x8 qf[2][4];
   f32x4 oacc[2][8];
-  float mrun[2], lrun[2];
+  float mref[2], lrun[2];     // reference max (log2 units) and running sum
   bool tval[2] = {false, false};
+  bf16x8 pprev[2];            // P of the previous key chunk; its PV product is pending
+  bool pend = false;
+  int pslot = 0;
+  bool fin = false;           // the pending chunk was its item's last: store O after its PV
+  bool fval0 = false, fval1 = false;
+  // (wave-uniform) first O row of this wave's query tiles in that item, its
+  // head, and the item's rows from that first row on
+  int fin_row = 0, fin_h = 0, fin_n = 0;
+
+  // O^T += V^T P^T for the pending chunk.  The V^T fragment (16 dh x 32 keys)
+  // of dh tile dt is two transposing reads: this lane addresses V row
+  // g4*8 + r*4 + l16/4 at dh dt*16 + 4*(l16%4); four reads per asm block.
+  auto pv_pending = [&]() __attribute__((always_inline)) {
+    const GS_LDS bf16* vs = (const GS_LDS bf16*)&ring[pslot * STAGE_ELEMS] + ATT_KC * DH;
+#pragma unroll
+    for (int quarter = 0; quarter < 4; ++quarter) {
+      const GS_LDS bf16* va[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int kr = g4 * 8 + r * 4 + (l16 >> 2);
+          const int e0 = (quarter * 2 + q) * 16 + 4 * (l16 & 3);
+          va[q * 2 + r] = vs + kr * DH + (((e0 >> 3) ^ swz_v(kr)) * 8) + (e0 & 7);
+        }
+      bf16x8 vf[2];
+      lds_read_tr_x4(va, vf);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int dt = quarter * 2 + q;
+        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[q], pprev[0], oacc[0][dt], 0, 0, 0);
+        if (tval[1])
+          oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[q], pprev[1], oacc[1][dt], 0, 0, 0);
+      }
+    }
+  };
+  // normalise and store the finished item's O (8 stores per valid tile)
+  auto store_fin = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if (tt == 0 ? !fval0 : !fval1) continue;
+      const float l = xsum_lanes16(xsum_lanes32(lrun[tt]));
+      const float inv = 1.f / l;
+      if (tt * 16 + l16 < fin_n) {
+        bf16* op = O + (size_t)(fin_row + tt * 16 + l16) * d + fin_h * DH + g4 * 4;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          bf16x4 o;
+          o[0] = to_bf16(oacc[tt][dt][0] * inv);
+          o[1] = to_bf16(oacc[tt][dt][1] * inv);
+          o[2] = to_bf16(oacc[tt][dt][2] * inv);
+          o[3] = to_bf16(oacc[tt][dt][3] * inv);
+          *(bf16x4*)(op + dt * 16) = o;
+        }
+      }
+      ops += 8;  // issued: lane l16 = 0 of a valid tile is in range
+    }
+  };
 
   for (int p = 0; comp.valid; ++p) {
     const int slot = p & (ATT_NST - 1);
     // this stage's copies (and everything before them) have landed
     wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - mark[0]));
-    stream_barrier();             // everyone's landed; everyone is done with stage p-1
+    stream_barrier();  // everyone's landed; everyone is done with stage p-2
     if (iss.valid) {
-      issue(iss, (p + ATT_NST - 1) & (ATT_NST - 1));  // refill the slot freed by stage p-1
+      issue(iss, (p + AHEAD) & (ATT_NST - 1));  // refill the slot of stage p-2
       cursor_next(iss, table, items, heads);
     }
 #pragma unroll
-    for (int i = 0; i < ATT_NST - 2; ++i) mark[i] = mark[i + 1];
-    mark[ATT_NST - 2] = ops;  // position p+NST-1 (if issued; otherwise never waited for)
+    for (int i = 0; i < AHEAD - 1; ++i) mark[i] = mark[i + 1];
+    mark[AHEAD - 1] = ops;  // position p+AHEAD (if issued; otherwise never waited for)
     const GS_LDS bf16* st = (const GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
+    const bool kstage = comp.s >= comp.nq;
+    const bool work = kstage && tval[0];
 
-    if (comp.s < comp.nq) {
-      // ---- query stage: the waves owning these 128 rows load their tiles ----
+    // ---- S^T = K Q^T for this chunk (32 keys) ----
+    // Tile kt row r feeds key perm_key(kt, r), so a lane holds keys
+    // g4*8 + kt*4 + i.  Tile 1 holds keys {4..7, 12..15, 20..23, 28..31}: it
+    // has a valid key iff kvalid > 4.
+    const int kvalid = min(ATT_KC, comp.L - (comp.s - comp.nq) * ATT_KC);
+    f32x4 s[2][2];
+    if (work) {
+      const bool two = kvalid > 4;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[0][kt] = s[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kt == 0 || two) {
+          const int kr = perm_key(kt, l16);
+          bf16x8 kf[4];
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+            kf[kc] = *(const GS_LDS bf16x8*)(st + kr * DH + ((kc * 4 + g4) ^ swz_k(kr)) * 8);
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+            s[0][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc], qf[0][kc], s[0][kt], 0, 0, 0);
+          if (tval[1]) {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+              s[1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc], qf[1][kc], s[1][kt], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // ---- the previous chunk's PV product (its V rows are still resident) and,
+    // if that chunk finished an item, the item's output ----
+    if (pend) {
+      pv_pending();
+      pend = false;
+    }
+    if (fin) {
+      store_fin();
+      fin = false;
+    }
+
+    if (!kstage) {
+      // ---- query stage: the waves owning these 64 rows load their tiles ----
       const int wfirst = comp.s * (ATT_QS / 32);  // 2 waves per query stage
       if (comp.s == 0) tval[0] = tval[1] = false;
       if (wave >= wfirst && wave < wfirst + ATT_QS / 32) {
@@ -249,125 +381,79 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
             const int lc = kc * 4 + g4;
             qf[tt][kc] = *(const GS_LDS bf16x8*)(st + rr * DH + (lc ^ swz_q(rr)) * 8);
           }
-          mrun[tt] = -INFINITY;
+          mref[tt] = -INFINITY;
           lrun[tt] = 0.f;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
-    } else if (tval[0]) {
-      // ---- key chunk (32 keys) ----
-      const int c = comp.s - comp.nq;
-      const int kvalid = min(ATT_KC, comp.L - c * ATT_KC);  // keys of this chunk in the block
-      const GS_LDS bf16* ks = st;
-      const GS_LDS bf16* vs = st + ATT_KC * DH;
-
-      // S^T for the two 16-key tiles; tile kt row r feeds key perm_key(kt, r)
-      f32x4 s[2][2];
-      bf16x8 kf[2][4];
+    } else if (work) {
+      // ---- softmax of this chunk ----
+      if (kvalid < ATT_KC) {  // masked keys (a block's partial last chunk) get -inf
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int kr = perm_key(kt, l16);
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          kf[kt][kc] = *(const GS_LDS bf16x8*)(ks + kr * DH + ((kc * 4 + g4) ^ swz_k(kr)) * 8);
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (g4 * 8 + kt * 4 + i >= kvalid) s[tt][kt][i] = -INFINITY;
       }
-      // tile 1 holds keys {4..7, 12..15, 20..23, 28..31}: it has a valid key iff kvalid > 4
-      const bool two = kvalid > 4;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[0][kt] = s[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (kt == 0 || two) {
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc)
-            s[0][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][kc], qf[0][kc], s[0][kt], 0, 0, 0);
-          if (tval[1]) {
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-              s[1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][kc], qf[1][kc], s[1][kt], 0, 0, 0);
-          }
-        }
-      }
-
-      // online softmax; P in the PV operand layout (lane holds keys g4*8 + j)
-      bf16x8 pf[2];
+      // row max of the chunk (raw scores) over the 4 lane groups of a query
+      float cmax[2];
+      bool grow = false;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        float mx = -INFINITY;
+        float mx = fmaxf(fmaxf(fmaxf(s[tt][0][0], s[tt][0][1]), fmaxf(s[tt][0][2], s[tt][0][3])),
+                         fmaxf(fmaxf(s[tt][1][0], s[tt][1][1]), fmaxf(s[tt][1][2], s[tt][1][3])));
+        mx = xmax_lanes16(xmax_lanes32(mx));
+        cmax[tt] = mx * scale_log2;
+        grow |= cmax[tt] > mref[tt] + LAZY_RESCALE;
+      }
+      // Lazy rescaling: the reference max only moves when a row max exceeds
+      // it by more than 2^LAZY_RESCALE (the previous chunk's PV is already in
+      // O), so P <= 2^LAZY_RESCALE and the common case leaves O alone.
+      if (__builtin_amdgcn_readfirstlane(__ballot(grow) != 0)) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int tt = 0; tt < 2; ++tt) {
+          const float mnew = fmaxf(mref[tt], cmax[tt]);
+          const float alpha = __builtin_amdgcn_exp2f(mref[tt] - mnew);
+          mref[tt] = mnew;
+          lrun[tt] *= alpha;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = g4 * 8 + kt * 4 + i;
-            const float v = key < kvalid ? s[tt][kt][i] * scale_log2 : -INFINITY;
-            s[tt][kt][i] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun[tt], mx);
-        const float alpha = exp2f(mrun[tt] - mnew);
-        mrun[tt] = mnew;
+          for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= alpha;
+        }
+      }
+      // P = exp2(s*scale - mref), rounded to bf16, in the PV operand layout
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
         float psum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bf16 pb = to_bf16(exp2f(s[tt][kt][i] - mnew));
+            const bf16 pb =
+                to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][kt][i], scale_log2, -mref[tt])));
             psum += to_f32(pb);
-            pf[tt][kt * 4 + i] = pb;
+            pprev[tt][kt * 4 + i] = pb;
           }
-        lrun[tt] = lrun[tt] * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= alpha;
+        lrun[tt] += psum;
       }
-
-      // O^T += V^T P^T.  The V^T fragment (16 dh x 32 keys) is two transposing
-      // reads: this lane addresses V row g4*8 + r*4 + l16/4 at dh
-      // dt*16 + 4*(l16%4).
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const GS_LDS bf16* va[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int kr = g4 * 8 + r * 4 + (l16 >> 2);
-          const int e0 = dt * 16 + 4 * (l16 & 3);
-          va[r] = vs + kr * DH + (((e0 >> 3) ^ swz_v(kr)) * 8) + (e0 & 7);
-        }
-        const bf16x8 vf = lds_read_tr_pair(va[0], va[1]);
-        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], oacc[0][dt], 0, 0, 0);
-        if (tval[1])
-          oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], oacc[1][dt], 0, 0, 0);
-      }
-
-      // ---- last chunk of the item: normalise and store ----
-      if (comp.s == comp.ns - 1) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          if (!tval[tt]) continue;
-          float l = lrun[tt];
-          l += __shfl_xor(l, 16);
-          l += __shfl_xor(l, 32);
-          const float inv = 1.f / l;
-          const int q = comp.q0 + wave * 32 + tt * 16 + l16;
-          if (q < comp.q0 + comp.qn) {
-            bf16* op = O + (size_t)(comp.row0 + q) * d + comp.h * DH + g4 * 4;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-              bf16x4 o;
-              o[0] = to_bf16(oacc[tt][dt][0] * inv);
-              o[1] = to_bf16(oacc[tt][dt][1] * inv);
-              o[2] = to_bf16(oacc[tt][dt][2] * inv);
-              o[3] = to_bf16(oacc[tt][dt][3] * inv);
-              *(bf16x4*)(op + dt * 16) = o;
-            }
-          }
-          ops += 8;  // issued by the lanes that store; counted per wave either way
-        }
+      pend = true;
+      pslot = slot;
+      if (comp.s == comp.ns - 1) {  // the item is done once this chunk's PV is in
+        fin = true;
+        fval0 = tval[0];
+        fval1 = tval[1];
+        fin_row = comp.row0 + comp.q0 + wave * 32;
+        fin_h = comp.h;
+        fin_n = comp.qn - wave * 32;
       }
     }
     cursor_next(comp, table, items, heads);
   }
+  // the stream's last chunk
+  if (pend) pv_pending();
+  if (fin) store_fin();
 }
 
 static int g_num_cus = 0;
