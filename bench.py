@@ -5,6 +5,8 @@ output projection with residual) over the whole packed batch, inputs already
 resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --copy-calibration MB   (plain device copy of MB MiB, for
+                                           scaling HBM byte counters)
 """
 from __future__ import annotations
 
@@ -89,6 +91,8 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=workloads.WORKLOAD_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device-to-device copy of MB MiB, 5 times")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -99,6 +103,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        # Reference kernel for the byte counters: reads and writes exactly
+        # `nbytes` per launch.
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
+        return
 
     w = workloads.WORKLOADS[args.workload]
     case = workloads.build_case(w, layers=w.layers)
