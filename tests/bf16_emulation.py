@@ -1,0 +1,58 @@
+"""CPU emulation of the bf16 path's rounding points, for setting a tolerance.
+
+Test-side tool, not the oracle and not the product: it repeats the sub-layer
+(IBM model card, "Model Architecture" (1): block attention over 4-second
+blocks; sequence packing with non-causal attention from the card's usage
+section) in fp64, but rounds to bf16 (round to nearest even) exactly where
+the bf16 GPU path rounds:
+
+  * Q, K, V after the projection,
+  * the unnormalised softmax weights p = exp(z - m) before the P.V product
+    (the sum of weights is taken over the rounded values),
+  * O = (P.V) / sum(p),
+  * out = x + O.Wo^T.
+
+Everything between those points is exact (fp64), so the difference between
+this emulation and the fp64 oracle is the error the rounding points alone
+cause.  It is used where that error is large by nature (the 16-layer chain,
+whose activations grow layer by layer and whose softmax sharpens).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+
+def _bf16(a: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).double().numpy()
+
+
+def block_mhsa_rows(x, cu, wqkv, wo, block_frames: int, heads: int, mask: np.ndarray) -> np.ndarray:
+    """Emulated output for the rows of every block that has a row selected in
+    `mask` (NaN elsewhere).  x, wqkv, wo: bf16 torch tensors on the CPU."""
+    xd = x.double().numpy()
+    w1 = wqkv.double().numpy()
+    w2 = wo.double().numpy()
+    n, d = xd.shape
+    dh = d // heads
+    out = np.full((n, d), np.nan)
+    cu = np.asarray(cu, dtype=np.int64)
+    for s in range(len(cu) - 1):
+        for a in range(int(cu[s]), int(cu[s + 1]), block_frames):
+            b = min(a + block_frames, int(cu[s + 1]))
+            if not mask[a:b].any():
+                continue
+            xb = xd[a:b]
+            qkv = _bf16(xb @ w1.T)
+            o = np.empty((b - a, d))
+            for h in range(heads):
+                q = qkv[:, h * dh:(h + 1) * dh]
+                k = qkv[:, d + h * dh:d + (h + 1) * dh]
+                v = qkv[:, 2 * d + h * dh:2 * d + (h + 1) * dh]
+                z = (q @ k.T) / math.sqrt(dh)
+                p = _bf16(np.exp(z - z.max(axis=1, keepdims=True)))
+                o[:, h * dh:(h + 1) * dh] = (p @ v) / p.sum(axis=1, keepdims=True)
+            out[a:b] = _bf16(xb + _bf16(o) @ w2.T)
+    return out

@@ -166,6 +166,41 @@ def test_workload_full_size_sampled(orc, name):
         assert torch.equal(one, out[a:b]), f"sequence {s} differs when run alone"
 
 
+def test_workload_chain16_teacher_forced(orc):
+    """16 layers with independent weights, each fed the previous layer's GPU output.
+
+    Without normalisation the chain amplifies: activations grow layer by layer
+    and the softmax sharpens, so the rounding of Q and K to bf16 alone moves
+    later layers' outputs by more than 2e-2 of their RMS.  Each layer is
+    therefore checked teacher-forced (the oracle gets the exact bf16 input the
+    GPU layer got), layer 1 against the plain bf16 bar and every later layer
+    against max(2e-2, 2 x the error of a CPU emulation of the same bf16
+    rounding points)."""
+    from tests import bf16_emulation
+
+    G.print_case("bf16_b128_chain16")
+    case = workloads.build_case(workloads.WORKLOADS["bf16_b128_chain16"])
+    assert len(case.weights) == 16
+    mask = G.sample_mask(case.lengths, case.block_frames, n_random=3, seed=2)
+    sel = mask.astype(bool)
+    cu = torch.from_numpy(case.cu).to(G.dev())
+    cur = case.x.to(G.dev())
+    for layer, (wqkv, wo) in enumerate(case.weights):
+        out = G.run(cur, cu, wqkv.to(G.dev()), wo.to(G.dev()), case.block_frames, case.heads)
+        inp = cur.cpu()
+        ref = orc.block_mhsa(inp, case.cu, wqkv, wo, case.block_frames, case.heads, mask=mask)
+        emu = bf16_emulation.block_mhsa_rows(inp, case.cu, wqkv, wo, case.block_frames, case.heads,
+                                             mask)
+        err = G.rel_err(out.double().cpu().numpy()[sel], ref[sel])
+        err_emu = G.rel_err(emu[sel], ref[sel])
+        bar = G.BF16_TOL if layer == 0 else max(G.BF16_TOL, 2.0 * err_emu)
+        rms = float(np.sqrt(np.mean(ref[sel] ** 2)))
+        print(f"  layer {layer + 1:2d}: rms(out)={rms:.3f} err={err:.3e} emulated={err_emu:.3e} "
+              f"bar={bar:.3e}", flush=True)
+        assert np.isfinite(err) and err <= bar, (layer, err, bar)
+        cur = out
+
+
 # ---------------------------------------------------------------------------
 # ragged and degenerate shapes, element by element
 
