@@ -13,12 +13,14 @@ LIB = os.path.join(HERE, "libgsattn.so")
 
 SOURCES = ["gsattn_api.hip", "gemm_bf16.hip", "gemm_f32.hip", "attn_bf16.hip", "attn_f32.hip"]
 
+# Per-source code-generation options (none at present).
+SOURCE_FLAGS: dict = {}
+
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # keep the compiler from forming packed-fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
@@ -30,9 +32,7 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(out: str = LIB, verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", out + ".tmp"]
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,6 +42,19 @@ def build(out: str = LIB, verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(out: str = LIB, verbose: bool = False) -> str:
+    """Compile every source to an object (with its own options), then link."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        _run([hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), f"-I{INCLUDE}", f"-I{CSRC}",
+              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"], verbose)
     os.replace(out + ".tmp", out)
     return out
 

@@ -136,7 +136,7 @@ __device__ __forceinline__ void swap_lo_hi(unsigned& x, unsigned& y) {
   y = s[1];
 }
 
-template <int BN, int BK, int NST, int EARLY, int SPLIT, bool RESID>
+template <int BN, int BK, int NST, bool DEFER, int EARLY, int SPLIT, bool RESID>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* R, bf16* C,
     int M, int Nc, int K) {
@@ -197,7 +197,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
 
   // ---- copy side: the next (tile, step) to issue ----
   int ops = 0;         // vector-memory ops this wave has issued
-  int mark[NST];       // ops right after the copies of each of the next NST steps
+  // Steps in the ring ahead of the one being computed.  Without DEFER a
+  // stage is refilled as soon as it is freed (in the last chunk of a step);
+  // with DEFER its copies are spread over all chunks of the following step,
+  // so one stage is always being refilled and NST-1 are ready or in flight.
+  constexpr int DEPTH = DEFER ? NST - 1 : NST;
+  int mark[DEPTH];     // ops right after the copies of each of the next DEPTH steps
   int is_k = 0, is_step = 0, is_panel, is_col, is_slot = 0;
   tile_of(0, is_panel, is_col);
   if (is_panel < 0) return;  // uniform: no work for this workgroup
@@ -219,9 +224,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
     else
       cpB.issue_one(j - CopyA::INSTR, tB + is_step * BK, K, stage_b(is_slot), wave);
   };
-  // after all LPS copies of a step
+  // after all LPS copies of a step (the caller counts them in ops)
   auto advance_issue = [&]() __attribute__((always_inline)) {
-    ops += LPS;
     is_slot = is_slot + 1 == NST ? 0 : is_slot + 1;
     if (++is_step == KT) {
       is_step = 0;
@@ -290,13 +294,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
     }
   };
 
-  // ---- prologue: the first NST steps ----
+  // ---- prologue: the first DEPTH steps ----
 #pragma unroll
-  for (int s = 0; s < NST; ++s) {
+  for (int s = 0; s < DEPTH; ++s) {
     if (is_panel >= 0) {
 #pragma unroll
       for (int j = 0; j < LPS; ++j) copy_one(j);
       advance_issue();
+      ops += LPS;
     }
     mark[s] = ops;
   }
@@ -328,26 +333,32 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
       constexpr int NS = decltype(ns_tag)::value;  // output pieces stored in this step
       constexpr int NM = TI * TJ, NR = TI + TJ;
       if (kt == rstep) load_residual(m0, n0);
+      // DEFER: the stage freed in the previous step is refilled during this one
+      bool do_issue = DEFER && is_panel >= 0;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int p = kk & 1;
         const bool last = kk == KK - 1;
         wait_lds();  // chunk kk's fragments are in registers
         int nslot = cm_slot;
-        bool do_issue = false;
         if (last) {
           // the next step landed (this wave's copies), then for everyone;
           // everyone is done reading this step's stage
           gemm_wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - mark[1]));
           gemm_barrier();
-          do_issue = is_panel >= 0;
+          if (!DEFER) do_issue = is_panel >= 0;
           nslot = cm_slot + 1 == NST ? 0 : cm_slot + 1;
         }
         const int nkk = last ? 0 : kk + 1;
         const int lo = frag_row * BK + ((nkk * 2 + half) ^ G::swz(frag_row)) * 8;
         const GS_LDS bf16* as = stage_a(nslot) + wm * 128 * BK + lo;
         const GS_LDS bf16* bs = stage_b(nslot) + wn * WN * BK + lo;
-        const int nside = NR + (last ? LPS + NS : 0);
+        // side instructions of this chunk: fragment reads, copies c0..c1-1,
+        // output pieces s0..s1-1
+        const int c0 = DEFER ? kk * LPS / KK : 0;
+        const int c1 = DEFER ? (kk + 1) * LPS / KK : (last ? LPS : 0);
+        const int s0 = kk * NS / KK, s1 = (kk + 1) * NS / KK;
+        const int nside = NR + (c1 - c0) + (s1 - s0);
 #pragma unroll
         for (int n = 0; n < NM; ++n) {
           acc[n / TJ][n % TJ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -358,20 +369,26 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
               af[p ^ 1][si] = *(const GS_LDS bf16x8*)(as + si * 32 * BK);
             } else if (si < NR) {
               bfr[p ^ 1][si - TI] = *(const GS_LDS bf16x8*)(bs + (si - TI) * 32 * BK);
-            } else if (si < NR + LPS) {
-              if (do_issue) copy_one(si - NR);
+            } else if (si < NR + (c1 - c0)) {
+              if (do_issue) copy_one(c0 + si - NR);
             } else if (st_active) {
-              store_piece(q0 + si - NR - LPS);
+              store_piece(q0 + s0 + si - NR - (c1 - c0));
             }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
         if (last) {
-          if (do_issue) advance_issue();
+          // In issue order, this step's copies end before the pieces of its
+          // last chunk: the mark goes there.
+          if (do_issue) {
+            advance_issue();
+            ops += LPS;
+          }
+          if (st_active) ops += s0;
 #pragma unroll
-          for (int i = 0; i < NST - 1; ++i) mark[i] = mark[i + 1];
-          mark[NST - 1] = ops;
-          if (st_active) ops += NS;
+          for (int i = 0; i < DEPTH - 1; ++i) mark[i] = mark[i + 1];
+          mark[DEPTH - 1] = ops;
+          if (st_active) ops += NS - s0;
           cm_slot = nslot;
         }
       }
@@ -479,7 +496,7 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int 
   // 3d = 384 * heads is always a multiple of 192
   const int Nc = 3 * d;
   const int mt = (M + GEMM_BM - 1) / GEMM_BM;
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<192, 64, 2, 0, 12, false>), dim3(gemm_persistent_grid(mt * (Nc / 192))),
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<192, 64, 2, false, 0, 12, false>), dim3(gemm_persistent_grid(mt * (Nc / 192))),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)x, (const bf16*)wqkv,
                      (const bf16*)nullptr, (bf16*)qkv, M, Nc, d);
   return hipGetLastError();
@@ -488,7 +505,7 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int 
 hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
                                 int d, hipStream_t stream) {
   const int mt = (M + GEMM_BM - 1) / GEMM_BM;
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<128, 64, 3, 0, 8, true>), dim3(gemm_persistent_grid(mt * (d / 128))),
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<128, 64, 3, false, 0, 8, true>), dim3(gemm_persistent_grid(mt * (d / 128))),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)o, (const bf16*)wo,
                      (const bf16*)x, (bf16*)out, M, d, d);
   return hipGetLastError();
