@@ -7,11 +7,11 @@
 // reading Q|K|V from the projection output qkv[N][3d] and writing O[N][d].
 //
 // Work item = (unit, head), unit = (block, group of up to 256 query rows),
-// taken from a unit table built on the device from cu_seqlens (read here with
-// scalar loads).
+// taken from a unit table built on the device from cu_seqlens, sorted by cost
+// (read here with scalar loads).
 //
-// Persistent workgroups, one per CU (8 waves): workgroup w processes items
-// w, w + G, w + 2G, ...  All operands stream through one LDS ring of NST
+// Persistent workgroups, one per CU (8 waves), each taking one item per round
+// in snake order over the sorted table.  All operands stream through one LDS ring of NST
 // stages of 16 KB filled by 16-byte global->LDS direct copies: an item
 // contributes its query stages (64 rows each), then its key chunks (32 K
 // rows + 32 V rows).  Copies run NST-1 stages ahead of the math, across item
@@ -144,9 +144,12 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 }
 #undef GS_VMCNT
 
-// Position in a workgroup's stream of stages.
+// Position in a workgroup's stream of stages.  Items are taken in snake
+// order over the cost-sorted unit table: round r gives this workgroup the
+// item at position r*G + w (even r) or r*G + G-1-w (odd r).
 struct Cursor {
-  int v;       // work item (unit * heads + head)
+  int r;       // round
+  int v;       // work item (unit position * heads + head)
   bool valid;  // false past the workgroup's last item
   int row0, L, q0, qn, h;
   int s;       // stage index inside the item
@@ -155,6 +158,7 @@ struct Cursor {
 
 __device__ __forceinline__ void cursor_load(Cursor& c, const int4* __restrict__ table, int items,
                                             int heads) {
+  c.v = c.r * (int)gridDim.x + ((c.r & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x);
   c.valid = c.v < items;
   c.s = 0;
   if (c.valid) {
@@ -170,7 +174,7 @@ __device__ __forceinline__ void cursor_load(Cursor& c, const int4* __restrict__ 
 __device__ __forceinline__ void cursor_next(Cursor& c, const int4* __restrict__ table, int items,
                                             int heads) {
   if (++c.s == c.ns) {
-    c.v += gridDim.x;
+    ++c.r;
     cursor_load(c, table, items, heads);
   }
 }
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   // resident for one more iteration, because its PV product is done then.
   constexpr int AHEAD = ATT_NST - 2;
   Cursor comp, iss;
-  comp.v = blockIdx.x;
+  comp.r = 0;
   cursor_load(comp, table, items, heads);
   if (!comp.valid) return;  // uniform over the workgroup
   iss = comp;
@@ -469,8 +473,7 @@ hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long lo
       n = 256;
     g_num_cus = n;
   }
-  hipLaunchKernelGGL(build_unit_table_kernel<ATT_QG>, dim3(1), dim3(1024), 0, stream, cu, S, B,
-                     (int4*)table);
+  build_unit_table_kernel<ATT_QG, ATT_QS, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(cu, S, B, (int4*)table);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long items = (long long)attn_unit_bound(N, S, B, ATT_QG) * heads;

@@ -70,45 +70,70 @@ __device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnU
 }
 
 // Unit table for kernels that read their units with scalar loads.
-// table[0].x = number of units; table[1 + u] = {row0, L, q0, qn} of unit u.
+// table[0].x = number of units; table[1 + i] = {row0, L, q0, qn} of the i-th
+// unit in order of decreasing cost, the cost being the number of ring stages
+// a unit takes, ceil(qn/QS) + ceil(L/KC) (capped at 1023; the order of units
+// of equal cost is unspecified).  With the costliest units first, a
+// persistent kernel that deals them out in a snake order (round r hands
+// position r*G + w to workgroup w for even r, to G-1-w for odd r) keeps its
+// workgroups within about one unit of each other.
 // Every unit holds at least one row, so N + 1 entries always suffice.
-// One workgroup; sequences are scanned 1024 at a time (block-wide prefix sum).
-template <int QG>
+// One workgroup; a counting sort over the cost: a histogram pass and a
+// placement pass over the sequences, 1024 sequences at a time.
+template <int QG, int QS, int KC>
 __global__ __launch_bounds__(1024) void build_unit_table_kernel(const int* __restrict__ cu, int S,
                                                                int B, int4* __restrict__ table) {
-  __shared__ int scan[1024];
+  constexpr int BINS = 1024;
+  __shared__ int next[BINS];  // per cost bin: count, then next free position
+  __shared__ int scan[BINS];
   const int tid = threadIdx.x;
   const int upb = (B - 1) / QG + 1;
-  int base = 0;
-  for (int c0 = 0; c0 < S; c0 += 1024) {
-    const int s = c0 + tid;
-    int len = 0;
-    if (s < S) len = cu[s + 1] - cu[s];
-    const int n = units_of_seq<QG>(len, B, upb);
-    scan[tid] = n;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int y = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += y;
-      __syncthreads();
-    }
-    const int excl = base + scan[tid] - n;
-    if (n > 0) {
-      const int start = cu[s];
-      const int nb = (len - 1) / B + 1;
-      for (int v = 0; v < n; ++v) {
-        int j = v / upb;
-        if (j > nb - 1) j = nb - 1;
-        const int g = v - j * upb;
-        const int L = (j < nb - 1) ? B : len - (nb - 1) * B;
-        table[1 + excl + v] = make_int4(start + j * B, L, g * QG, min(QG, L - g * QG));
+  next[tid] = 0;
+  __syncthreads();
+  // the v-th unit of a sequence of `len` rows starting at `start`
+  auto unit = [&](int start, int len, int v) {
+    const int nb = (len - 1) / B + 1;
+    int j = v / upb;
+    if (j > nb - 1) j = nb - 1;
+    const int g = v - j * upb;
+    const int L = (j < nb - 1) ? B : len - (nb - 1) * B;
+    return make_int4(start + j * B, L, g * QG, min(QG, L - g * QG));
+  };
+  auto bin_of = [&](int4 e) {  // bin 0 holds the costliest units
+    const int cost = (e.w + QS - 1) / QS + (e.y + KC - 1) / KC;
+    return BINS - 1 - min(cost, BINS - 1);
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int c0 = 0; c0 < S; c0 += 1024) {
+      const int s = c0 + tid;
+      int len = 0;
+      if (s < S) len = cu[s + 1] - cu[s];
+      const int n = units_of_seq<QG>(len, B, upb);
+      if (n > 0) {
+        const int start = cu[s];
+        for (int v = 0; v < n; ++v) {
+          const int4 e = unit(start, len, v);
+          const int pos = atomicAdd(&next[bin_of(e)], 1);
+          if (pass == 1) table[1 + pos] = e;
+        }
       }
     }
-    base += scan[1023];
     __syncthreads();
+    if (pass == 0) {  // counts -> first position of each bin (exclusive scan)
+      const int n = next[tid];
+      scan[tid] = n;
+      __syncthreads();
+      for (int off = 1; off < BINS; off <<= 1) {  // inclusive Hillis-Steele scan
+        const int y = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += y;
+        __syncthreads();
+      }
+      next[tid] = scan[tid] - n;
+      if (tid == 0) table[0] = make_int4(scan[BINS - 1], 0, 0, 0);
+      __syncthreads();
+    }
   }
-  if (tid == 0) table[0] = make_int4(base, 0, 0, 0);
 }
 
 // Upper bound on the number of units of N rows in S sequences:
