@@ -254,8 +254,14 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   // per-wave query state: rows 32*wave + 16*tt + lane%16 of the current item
   bf16x8 qf[2][4];
   f32x4 oacc[2][8];
-  float mref[2], lrun[2];     // reference max (log2 units) and running sum
+  // Running row sums of P, kept by the matrix unit: lsum[tt] += 1 * P^T, so
+  // each of the four values of a lane holds the sum for query lane%16.
+  f32x4 lsum[2];
+  // reference max per query in log2 units, and the raw score above which it
+  // has to move: thr = (mref + LAZY_RESCALE) / scale_log2
+  float mref[2] = {0.f, 0.f}, thr[2] = {INFINITY, INFINITY};
   bool tval[2] = {false, false};
+  bool fresh = false;         // the next key chunk is its item's first
   bf16x8 pprev[2];            // P of the previous key chunk; its PV product is pending
   bool pend = false;
   int pslot = 0;
@@ -264,23 +270,43 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   // (wave-uniform) first O row of this wave's query tiles in that item, its
   // head, and the item's rows from that first row on
   int fin_row = 0, fin_h = 0, fin_n = 0;
+  const float inv_scale_log2 = 1.f / scale_log2;
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
 
-  // O^T += V^T P^T for the pending chunk.  The V^T fragment (16 dh x 32 keys)
-  // of dh tile dt is two transposing reads: this lane addresses V row
-  // g4*8 + r*4 + l16/4 at dh dt*16 + 4*(l16%4); four reads per asm block.
+  // Per-lane LDS byte offsets inside a stage (the slot base is added per stage).
+  //   K: row perm_key(kt, lane%16) at chunk kc*4 + lane/16; tile kt = 1 is 4
+  //      rows (1 KB) further on with the same swizzle.
+  //   V: rows g4*8 + r*4 + lane%16/4 at dh (quarter*2+q)*16 + 4*(lane%16%4);
+  //      r = 1 is 4 rows further on with the same swizzle.
+  unsigned koff[4], voff[8];
+  {
+    const int kr = perm_key(0, l16);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) koff[kc] = (unsigned)(kr * DH + ((kc * 4 + g4) ^ swz_k(kr)) * 8) * 2u;
+    const int vr = g4 * 8 + (l16 >> 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e0 = j * 16 + 4 * (l16 & 3);
+      voff[j] = (unsigned)(ATT_KC * DH + vr * DH + (((e0 >> 3) ^ swz_v(vr)) * 8) + (e0 & 7)) * 2u;
+    }
+  }
+  const unsigned ring_base = (unsigned)(uintptr_t)(GS_LDS bf16*)ring;
+
+  // O^T += V^T P^T and lsum += 1 P^T for the pending chunk.  The V^T fragment
+  // (16 dh x 32 keys) of dh tile dt is two transposing reads; four reads per
+  // asm block.
   auto pv_pending = [&]() __attribute__((always_inline)) {
-    const GS_LDS bf16* vs = (const GS_LDS bf16*)&ring[pslot * STAGE_ELEMS] + ATT_KC * DH;
+    const unsigned vb = ring_base + (unsigned)pslot * (STAGE_ELEMS * 2);
 #pragma unroll
     for (int quarter = 0; quarter < 4; ++quarter) {
       const GS_LDS bf16* va[4];
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int kr = g4 * 8 + r * 4 + (l16 >> 2);
-          const int e0 = (quarter * 2 + q) * 16 + 4 * (l16 & 3);
-          va[q * 2 + r] = vs + kr * DH + (((e0 >> 3) ^ swz_v(kr)) * 8) + (e0 & 7);
-        }
+        for (int r = 0; r < 2; ++r)
+          va[q * 2 + r] = (const GS_LDS bf16*)(uintptr_t)(vb + voff[quarter * 2 + q] + r * (4 * DH * 2));
       bf16x8 vf[2];
       lds_read_tr_x4(va, vf);
 #pragma unroll
@@ -291,14 +317,15 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[q], pprev[1], oacc[1][dt], 0, 0, 0);
       }
     }
+    lsum[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[0], lsum[0], 0, 0, 0);
+    if (tval[1]) lsum[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[1], lsum[1], 0, 0, 0);
   };
   // normalise and store the finished item's O (8 stores per valid tile)
   auto store_fin = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       if (tt == 0 ? !fval0 : !fval1) continue;
-      const float l = xsum_lanes16(xsum_lanes32(lrun[tt]));
-      const float inv = 1.f / l;
+      const float inv = 1.f / lsum[tt][0];
       if (tt * 16 + l16 < fin_n) {
         bf16* op = O + (size_t)(fin_row + tt * 16 + l16) * d + fin_h * DH + g4 * 4;
 #pragma unroll
@@ -327,6 +354,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < AHEAD - 1; ++i) mark[i] = mark[i + 1];
     mark[AHEAD - 1] = ops;  // position p+AHEAD (if issued; otherwise never waited for)
+    const unsigned sb = ring_base + (unsigned)slot * (STAGE_ELEMS * 2);
     const GS_LDS bf16* st = (const GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
     const bool kstage = comp.s >= comp.nq;
     const bool work = kstage && tval[0];
@@ -343,11 +371,10 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
       for (int kt = 0; kt < 2; ++kt) {
         s[0][kt] = s[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (kt == 0 || two) {
-          const int kr = perm_key(kt, l16);
           bf16x8 kf[4];
 #pragma unroll
           for (int kc = 0; kc < 4; ++kc)
-            kf[kc] = *(const GS_LDS bf16x8*)(st + kr * DH + ((kc * 4 + g4) ^ swz_k(kr)) * 8);
+            kf[kc] = *(const GS_LDS bf16x8*)(uintptr_t)(sb + koff[kc] + kt * (4 * DH * 2));
 #pragma unroll
           for (int kc = 0; kc < 4; ++kc)
             s[0][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc], qf[0][kc], s[0][kt], 0, 0, 0);
@@ -374,7 +401,10 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     if (!kstage) {
       // ---- query stage: the waves owning these 64 rows load their tiles ----
       const int wfirst = comp.s * (ATT_QS / 32);  // 2 waves per query stage
-      if (comp.s == 0) tval[0] = tval[1] = false;
+      if (comp.s == 0) {
+        tval[0] = tval[1] = false;
+        fresh = true;
+      }
       if (wave >= wfirst && wave < wfirst + ATT_QS / 32) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -385,10 +415,6 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
             const int lc = kc * 4 + g4;
             qf[tt][kc] = *(const GS_LDS bf16x8*)(st + rr * DH + (lc ^ swz_q(rr)) * 8);
           }
-          mref[tt] = -INFINITY;
-          lrun[tt] = 0.f;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
     } else if (work) {
@@ -402,46 +428,47 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
             for (int i = 0; i < 4; ++i)
               if (g4 * 8 + kt * 4 + i >= kvalid) s[tt][kt][i] = -INFINITY;
       }
-      // row max of the chunk (raw scores) over the 4 lane groups of a query
-      float cmax[2];
-      bool grow = false;
+      // this lane's max raw score per query tile
+      float lmax[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float mx = fmaxf(fmaxf(fmaxf(s[tt][0][0], s[tt][0][1]), fmaxf(s[tt][0][2], s[tt][0][3])),
+      for (int tt = 0; tt < 2; ++tt)
+        lmax[tt] = fmaxf(fmaxf(fmaxf(s[tt][0][0], s[tt][0][1]), fmaxf(s[tt][0][2], s[tt][0][3])),
                          fmaxf(fmaxf(s[tt][1][0], s[tt][1][1]), fmaxf(s[tt][1][2], s[tt][1][3])));
-        mx = xmax_lanes16(xmax_lanes32(mx));
-        cmax[tt] = mx * scale_log2;
-        grow |= cmax[tt] > mref[tt] + LAZY_RESCALE;
-      }
-      // Lazy rescaling: the reference max only moves when a row max exceeds
+      // Lazy rescaling: the reference max only moves when some score exceeds
       // it by more than 2^LAZY_RESCALE (the previous chunk's PV is already in
-      // O), so P <= 2^LAZY_RESCALE and the common case leaves O alone.
-      if (__builtin_amdgcn_readfirstlane(__ballot(grow) != 0)) {
+      // O), so P <= 2^LAZY_RESCALE and the common case needs no cross-lane
+      // reduction and leaves O alone.  An item's first chunk sets it.
+      const bool grow = (lmax[0] > thr[0]) | (lmax[1] > thr[1]);
+      if (fresh || __builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const float mnew = fmaxf(mref[tt], cmax[tt]);
+          // the chunk's row max over the 4 lane groups of a query
+          const float cmax = xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2;
+          const float mnew = fresh ? cmax : fmaxf(mref[tt], cmax);
           const float alpha = __builtin_amdgcn_exp2f(mref[tt] - mnew);
           mref[tt] = mnew;
-          lrun[tt] *= alpha;
+          thr[tt] = (mnew + LAZY_RESCALE) * inv_scale_log2;
+          if (fresh) {  // the accumulators still hold the previous item's values
+            lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= alpha;
+            for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          } else {
+            lsum[tt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= alpha;
+          }
         }
+        fresh = false;
       }
       // P = exp2(s*scale - mref), rounded to bf16, in the PV operand layout
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float psum = 0.f;
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bf16 pb =
+          for (int i = 0; i < 4; ++i)
+            pprev[tt][kt * 4 + i] =
                 to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][kt][i], scale_log2, -mref[tt])));
-            psum += to_f32(pb);
-            pprev[tt][kt * 4 + i] = pb;
-          }
-        lrun[tt] += psum;
-      }
       pend = true;
       pslot = slot;
       if (comp.s == comp.ns - 1) {  // the item is done once this chunk's PV is in
