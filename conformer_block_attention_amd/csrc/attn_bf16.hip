@@ -39,15 +39,21 @@
 
 namespace gs {
 
-constexpr int ATT_THREADS = 512;
-constexpr int ATT_WAVES = ATT_THREADS / 64;
-constexpr int ATT_QG = 256;          // query rows per unit (8 waves x 32)
+#ifndef ATT_WAVES_CFG
+#define ATT_WAVES_CFG 8
+#endif
+constexpr int ATT_WAVES = ATT_WAVES_CFG;
+constexpr int ATT_THREADS = ATT_WAVES * 64;
+constexpr int ATT_QT = 16 / ATT_WAVES;  // 16-row query tiles per wave
+constexpr int ATT_QW = 16 * ATT_QT;  // query rows per wave
+constexpr int ATT_QG = ATT_WAVES * ATT_QW;  // query rows per unit (4 waves x 64)
 constexpr int ATT_QS = 64;           // query rows per query stage
+constexpr int ATT_WPQ = ATT_QS / ATT_QW;  // waves served by one query stage
 constexpr int ATT_KC = 32;           // keys per key chunk
 constexpr int DH = 128;
 constexpr int ATT_NST = 8;           // ring stages
 constexpr int STAGE_ELEMS = 8192;    // 16 KB: 64 rows of 128 bf16
-constexpr int COPIES = 2;            // 16-byte copies per lane per stage
+constexpr int COPIES = 16 / ATT_WAVES;  // 1 KB wave copies per wave per stage
 
 // LDS rows are 128 bf16 = 256 B = 16 chunks of 16 B, one full window of the
 // 64 four-byte banks; chunk c of row r is stored at physical chunk c ^ swz(r)
@@ -66,28 +72,76 @@ __device__ __forceinline__ int perm_key(int kt, int r) {
   return (kt >> 1) * 32 + (r >> 2) * 8 + (kt & 1) * 4 + (r & 3);
 }
 
-// Four transposing LDS reads (ds_read_b64_tr_b16) and a wait for them, in one
-// asm block, so the results are complete when it ends.  (Through the builtin,
-// the compiler makes every such read wait for all in-flight global->LDS
-// copies, which would drain the ring; ordering against those copies is
-// enforced by the explicit waits and barriers of the stream loop.)
-__device__ __forceinline__ void lds_read_tr_x4(const GS_LDS bf16* const* p, bf16x8* out) {
+// The V^T operands of one key chunk: sixteen transposing LDS reads
+// (ds_read_b64_tr_b16) and a wait for them, in one asm block, so the results
+// are complete when it ends.  Fragment dt is the pair of reads at a[dt] and
+// a[dt] + 1 KB (the second group of four V rows).  (Through the builtin, the
+// compiler makes every such read wait for all in-flight global->LDS copies,
+// which would drain the ring; ordering against those copies is enforced by
+// the explicit waits and barriers of the stream loop.)
+__device__ __forceinline__ void lds_read_vt_chunk(const unsigned* a, bf16x8* out) {
   typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-  unsigned long long r[4];
-  unsigned a[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = (unsigned)(uintptr_t)p[i];
+  unsigned long long r[16];
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:1024\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
-  out[0] = __builtin_bit_cast(bf16x8, u64x2{r[0], r[1]});
-  out[1] = __builtin_bit_cast(bf16x8, u64x2{r[2], r[3]});
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) out[dt] = __builtin_bit_cast(bf16x8, u64x2{r[2 * dt], r[2 * dt + 1]});
+}
+
+// Scores of two query tiles against the two 16-key tiles of a chunk:
+// s[t][kt] = sum over kc of K[kt][kc] Q[t][kc] (16x16x32 bf16 products, four
+// chained per tile, interleaved so that dependent products are four apart),
+// with the results in VGPRs for the VALU softmax that reads them.  (Left to
+// the compiler, every product of a kernel that may use more than 256
+// registers gets an AGPR destination, and each score would be moved out
+// again.)  The chains accumulate in place; the wait states at the end cover
+// a VALU read or write of a result right after the block (XDL write, then
+// VALU access of the same VGPRs: 4 passes + 4 on gfx950).
+__device__ __forceinline__ void score_tiles2(const bf16x8 (*k)[4], const bf16x8* q0, const bf16x8* q1,
+                                             f32x4& s00, f32x4& s01, f32x4& s10, f32x4& s11) {
+  asm volatile(
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %12, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %8, %12, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %4, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %8, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %13, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %9, %13, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %17, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %9, %17, %3\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %14, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %10, %14, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %6, %18, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %10, %18, %3\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %7, %15, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %11, %15, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %7, %19, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %11, %19, %3\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 3"
+      : "=&v"(s00), "=&v"(s01), "=&v"(s10), "=&v"(s11)
+      : "v"(k[0][0]), "v"(k[0][1]), "v"(k[0][2]), "v"(k[0][3]), "v"(k[1][0]), "v"(k[1][1]),
+        "v"(k[1][2]), "v"(k[1][3]), "v"(q0[0]), "v"(q0[1]), "v"(q0[2]), "v"(q0[3]), "v"(q1[0]),
+        "v"(q1[1]), "v"(q1[2]), "v"(q1[3]));
 }
 
 // Max / sum of a value over the lane pairs (l, l^32) and (l, l^16), with the
@@ -110,9 +164,10 @@ __device__ __forceinline__ float xsum_lanes16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The softmax reference max moves only when a row max exceeds it by more than
-// this many doublings (P stays <= 2^8, well inside bf16 and fp32 range).
-constexpr float LAZY_RESCALE = 8.f;
+// Scores may exceed an item's reference max by this many doublings before the
+// item is handed to the exact fallback: P <= 2^64, and O and the row sums of
+// at most 2^31 keys stay far inside fp32 range for any |V| < 2^32.
+constexpr float REF_HEADROOM = 64.f;
 
 // Workgroup barrier without a memory fence.  A fence would make every wave
 // wait for all of its outstanding global->LDS copies and global stores; the
@@ -180,8 +235,8 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int4* __restrict__ 
 }
 
 __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
-    const bf16* __restrict__ qkv, const int4* __restrict__ table, int heads, int d,
-    float scale_log2, bf16* __restrict__ O) {
+    const bf16* __restrict__ qkv, int4* __restrict__ table, unsigned long long* __restrict__ ovf,
+    int heads, int d, float scale_log2, bf16* __restrict__ O) {
   __shared__ __attribute__((aligned(1024))) bf16 ring[ATT_NST * STAGE_ELEMS];
 
   const int lane = threadIdx.x & 63;
@@ -199,8 +254,9 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   for (int i = 0; i < ATT_NST - 1; ++i) mark[i] = 0;
 
   // ---- copies of one stage into ring slot `slot` --------------------------
-  // 16 KB = 16 wave copies of 1 KB (4 rows of 256 B); wave w does copies w and
-  // w+8; lane -> row r0 + lane/16, physical chunk lane%16.
+  // 16 KB = 16 wave copies of 1 KB (4 rows of 256 B); wave w does copies
+  // w, w+4, w+8, w+12; lane -> row r0 + lane/16, physical chunk lane%16.  In a
+  // key stage rows 0..31 are the chunk's K rows and rows 32..63 its V rows.
   auto issue = [&](const Cursor& c, int slot) __attribute__((always_inline)) {
     GS_LDS bf16* dst = (GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
     const int pc = lane & 15;
@@ -216,12 +272,12 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         const int lc = pc ^ swz_q(rr);
         copy16_to_lds(qkv + (size_t)(c.row0 + q) * ld + c.h * DH + lc * 8, dst + r0 * DH);
       }
-    } else {           // key chunk: 32 K rows (copy 0) then 32 V rows (copy 1)
+    } else {           // key chunk: 32 K rows then 32 V rows
       const int k0 = (c.s - c.nq) * ATT_KC;
 #pragma unroll
       for (int j = 0; j < COPIES; ++j) {
-        const bool isv = j == 1;
         const int r0 = (j * ATT_WAVES + wave) * 4;
+        const bool isv = r0 >= ATT_KC;
         const int kr = (r0 + (lane >> 4)) & (ATT_KC - 1);
         int key = k0 + kr;
         key = key < c.L ? key : c.L - 1;
@@ -251,25 +307,12 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     mark[s] = ops;
   }
 
-  // per-wave query state: rows 32*wave + 16*tt + lane%16 of the current item
-  bf16x8 qf[2][4];
-  f32x4 oacc[2][8];
-  // Running row sums of P, kept by the matrix unit: lsum[tt] += 1 * P^T, so
-  // each of the four values of a lane holds the sum for query lane%16.
-  f32x4 lsum[2];
-  // reference max per query in log2 units, and the raw score above which it
-  // has to move: thr = (mref + LAZY_RESCALE) / scale_log2
-  float mref[2] = {0.f, 0.f}, thr[2] = {INFINITY, INFINITY};
-  bool tval[2] = {false, false};
-  bool fresh = false;         // the next key chunk is its item's first
-  bf16x8 pprev[2];            // P of the previous key chunk; its PV product is pending
-  bool pend = false;
-  int pslot = 0;
-  bool fin = false;           // the pending chunk was its item's last: store O after its PV
-  bool fval0 = false, fval1 = false;
-  // (wave-uniform) first O row of this wave's query tiles in that item, its
-  // head, and the item's rows from that first row on
-  int fin_row = 0, fin_h = 0, fin_n = 0;
+  // ---- per-wave query state: rows ATT_QW*wave + 16*tt + lane%16 of the item ----
+  bf16x8 qf[ATT_QT][4];
+#pragma unroll
+  for (int tt = 0; tt < ATT_QT; ++tt)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) qf[tt][kc] = bf16x8{};  // tiles without rows stay finite
   const float inv_scale_log2 = 1.f / scale_log2;
   bf16x8 ones;
 #pragma unroll
@@ -278,8 +321,8 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   // Per-lane LDS byte offsets inside a stage (the slot base is added per stage).
   //   K: row perm_key(kt, lane%16) at chunk kc*4 + lane/16; tile kt = 1 is 4
   //      rows (1 KB) further on with the same swizzle.
-  //   V: rows g4*8 + r*4 + lane%16/4 at dh (quarter*2+q)*16 + 4*(lane%16%4);
-  //      r = 1 is 4 rows further on with the same swizzle.
+  //   V: rows g4*8 + r*4 + lane%16/4 at dh dt*16 + 4*(lane%16%4); r = 1 is 4
+  //      rows (1 KB) further on with the same swizzle.
   unsigned koff[4], voff[8];
   {
     const int kr = perm_key(0, l16);
@@ -293,123 +336,89 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     }
   }
   const unsigned ring_base = (unsigned)(uintptr_t)(GS_LDS bf16*)ring;
+  constexpr unsigned STAGE_BYTES = STAGE_ELEMS * 2;
 
-  // O^T += V^T P^T and lsum += 1 P^T for the pending chunk.  The V^T fragment
-  // (16 dh x 32 keys) of dh tile dt is two transposing reads; four reads per
-  // asm block.
-  auto pv_pending = [&]() __attribute__((always_inline)) {
-    const unsigned vb = ring_base + (unsigned)pslot * (STAGE_ELEMS * 2);
-#pragma unroll
-    for (int quarter = 0; quarter < 4; ++quarter) {
-      const GS_LDS bf16* va[4];
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-          va[q * 2 + r] = (const GS_LDS bf16*)(uintptr_t)(vb + voff[quarter * 2 + q] + r * (4 * DH * 2));
-      bf16x8 vf[2];
-      lds_read_tr_x4(va, vf);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int dt = quarter * 2 + q;
-        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[q], pprev[0], oacc[0][dt], 0, 0, 0);
-        if (tval[1])
-          oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[q], pprev[1], oacc[1][dt], 0, 0, 0);
-      }
-    }
-    lsum[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[0], lsum[0], 0, 0, 0);
-    if (tval[1]) lsum[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[1], lsum[1], 0, 0, 0);
-  };
-  // normalise and store the finished item's O (8 stores per valid tile)
-  auto store_fin = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (tt == 0 ? !fval0 : !fval1) continue;
-      const float inv = 1.f / lsum[tt][0];
-      if (tt * 16 + l16 < fin_n) {
-        bf16* op = O + (size_t)(fin_row + tt * 16 + l16) * d + fin_h * DH + g4 * 4;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          bf16x4 o;
-          o[0] = to_bf16(oacc[tt][dt][0] * inv);
-          o[1] = to_bf16(oacc[tt][dt][1] * inv);
-          o[2] = to_bf16(oacc[tt][dt][2] * inv);
-          o[3] = to_bf16(oacc[tt][dt][3] * inv);
-          *(bf16x4*)(op + dt * 16) = o;
-        }
-      }
-      ops += 8;  // issued: lane l16 = 0 of a valid tile is in range
-    }
-  };
-
-  for (int p = 0; comp.valid; ++p) {
-    const int slot = p & (ATT_NST - 1);
-    // this stage's copies (and everything before them) have landed
+  // Start of stream position p: wait for its copies, meet the other waves, and
+  // refill the slot of position p-2 with position p+AHEAD.
+  int p = 0;
+  auto stage_begin = [&]() __attribute__((always_inline)) {
     wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - mark[0]));
     stream_barrier();  // everyone's landed; everyone is done with stage p-2
     if (iss.valid) {
-      issue(iss, (p + AHEAD) & (ATT_NST - 1));  // refill the slot of stage p-2
+      issue(iss, (p + AHEAD) & (ATT_NST - 1));
       cursor_next(iss, table, items, heads);
     }
 #pragma unroll
     for (int i = 0; i < AHEAD - 1; ++i) mark[i] = mark[i + 1];
     mark[AHEAD - 1] = ops;  // position p+AHEAD (if issued; otherwise never waited for)
-    const unsigned sb = ring_base + (unsigned)slot * (STAGE_ELEMS * 2);
-    const GS_LDS bf16* st = (const GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
-    const bool kstage = comp.s >= comp.nq;
-    const bool work = kstage && tval[0];
+  };
 
-    // ---- S^T = K Q^T for this chunk (32 keys) ----
-    // Tile kt row r feeds key perm_key(kt, r), so a lane holds keys
-    // g4*8 + kt*4 + i.  Tile 1 holds keys {4..7, 12..15, 20..23, 28..31}: it
-    // has a valid key iff kvalid > 4.
-    const int kvalid = min(ATT_KC, comp.L - (comp.s - comp.nq) * ATT_KC);
-    f32x4 s[2][2];
-    if (work) {
-      const bool two = kvalid > 4;
+  // V^T fragments of the chunk in ring slot `sl` (16 dh x 32 keys per dh tile).
+  auto read_vt = [&](int sl, bf16x8* vf) __attribute__((always_inline)) {
+    const unsigned vb = ring_base + (unsigned)sl * STAGE_BYTES;
+    unsigned va[8];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[0][kt] = s[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (kt == 0 || two) {
-          bf16x8 kf[4];
+    for (int dt = 0; dt < 8; ++dt) va[dt] = vb + voff[dt];
+    lds_read_vt_chunk(va, vf);
+  };
+  // S^T = K Q^T for the chunk in slot `sl`: tile kt row r feeds key
+  // perm_key(kt, r), so a lane holds keys g4*8 + kt*4 + i of its query.
+  auto scores = [&](int sl, f32x4 (*s)[2]) __attribute__((always_inline)) {
+    const unsigned sb = ring_base + (unsigned)sl * STAGE_BYTES;
+    bf16x8 kf[2][4];
 #pragma unroll
-          for (int kc = 0; kc < 4; ++kc)
-            kf[kc] = *(const GS_LDS bf16x8*)(uintptr_t)(sb + koff[kc] + kt * (4 * DH * 2));
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int kc = 0; kc < 4; ++kc)
-            s[0][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc], qf[0][kc], s[0][kt], 0, 0, 0);
-          if (tval[1]) {
+      for (int kc = 0; kc < 4; ++kc)
+        kf[kt][kc] = *(const GS_LDS bf16x8*)(uintptr_t)(sb + koff[kc] + kt * (4 * DH * 2));
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-              s[1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc], qf[1][kc], s[1][kt], 0, 0, 0);
-          }
-        }
-      }
+    for (int tt = 0; tt < ATT_QT; tt += 2)
+      score_tiles2(kf, qf[tt], qf[tt + 1], s[tt][0], s[tt][1], s[tt + 1][0], s[tt + 1][1]);
+  };
+  // Masks keys past the block end (a block's partial last chunk) and returns
+  // this lane's max raw score per query tile.
+  auto mask_max = [&](f32x4 (*s)[2], int kvalid, float* lmax) __attribute__((always_inline)) {
+    if (kvalid < ATT_KC) {
+#pragma unroll
+      for (int tt = 0; tt < ATT_QT; ++tt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (g4 * 8 + kt * 4 + i >= kvalid) s[tt][kt][i] = -INFINITY;
     }
+#pragma unroll
+    for (int tt = 0; tt < ATT_QT; ++tt)
+      lmax[tt] = fmaxf(fmaxf(fmaxf(s[tt][0][0], s[tt][0][1]), fmaxf(s[tt][0][2], s[tt][0][3])),
+                       fmaxf(fmaxf(s[tt][1][0], s[tt][1][1]), fmaxf(s[tt][1][2], s[tt][1][3])));
+  };
+  // P = exp2(s*scale - mref), rounded to bf16, in the PV operand layout
+  auto probs = [&](f32x4 (*s)[2], const float* mref, bf16x8* pn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tt = 0; tt < ATT_QT; ++tt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pn[tt][kt * 4 + i] =
+              to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][kt][i], scale_log2, -mref[tt])));
+  };
 
-    // ---- the previous chunk's PV product (its V rows are still resident) and,
-    // if that chunk finished an item, the item's output ----
-    if (pend) {
-      pv_pending();
-      pend = false;
-    }
-    if (fin) {
-      store_fin();
-      fin = false;
-    }
-
-    if (!kstage) {
-      // ---- query stage: the waves owning these 64 rows load their tiles ----
-      const int wfirst = comp.s * (ATT_QS / 32);  // 2 waves per query stage
-      if (comp.s == 0) {
-        tval[0] = tval[1] = false;
-        fresh = true;
-      }
-      if (wave >= wfirst && wave < wfirst + ATT_QS / 32) {
+  // ---- items ----
+  for (; comp.valid; ) {
+    const int nq = comp.nq;
+    const int nk = comp.ns - comp.nq;
+    const int nval = min(ATT_QW, comp.qn - wave * ATT_QW);  // this wave's query rows
+    const int row0 = comp.row0, L = comp.L, q0 = comp.q0, h = comp.h;
+    const int uidx = comp.v / heads;  // the unit's position in the table
+    // ---- query stages: wave w loads its rows at stage w / ATT_WPQ ----
+    for (int qs = 0; qs < nq; ++qs, ++p) {
+      stage_begin();
+      if (wave / ATT_WPQ == qs) {
+        const GS_LDS bf16* st = (const GS_LDS bf16*)&ring[(p & (ATT_NST - 1)) * STAGE_ELEMS];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int rr = (wave - wfirst) * 32 + tt * 16 + l16;
-          tval[tt] = (wave * 32 + tt * 16) < comp.qn;
+        for (int tt = 0; tt < ATT_QT; ++tt) {
+          const int rr = (wave % ATT_WPQ) * ATT_QW + tt * 16 + l16;
 #pragma unroll
           for (int kc = 0; kc < 4; ++kc) {
             const int lc = kc * 4 + g4;
@@ -417,74 +426,199 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           }
         }
       }
-    } else if (work) {
-      // ---- softmax of this chunk ----
-      if (kvalid < ATT_KC) {  // masked keys (a block's partial last chunk) get -inf
+    }
+    if (nval <= 0) {  // no rows for this wave: only keep the stream going
+      for (int kc = 0; kc < nk; ++kc, ++p) stage_begin();
+    } else {
+      f32x4 oacc[ATT_QT][8];
+      f32x4 lsum[ATT_QT];  // P row sums: lsum[tt] += 1 * P^T (4 copies per lane)
+      // Reference max per query: an integer in log2 units, fixed at the item's
+      // first chunk to ceil(that chunk's row max).  Later scores may exceed it
+      // by up to 2^REF_HEADROOM (P, O and the sums stay finite in bf16/fp32);
+      // a score beyond that flags the item for the exact fallback.  With an
+      // integer reference the bf16 rounding of P is the same as with the true
+      // row max.  thr is the raw score of that limit.
+      float mref[ATT_QT], thr[ATT_QT];
+      bf16x8 pprev[ATT_QT];  // P of the previous chunk, whose PV product is pending
+      int pslot;
+      bool flagged = false;  // (wave-uniform)
+      // ---- first key chunk: sets the reference, no PV product yet ----
+      {
+        stage_begin();
+        const int sl = p & (ATT_NST - 1);
+        f32x4 s[ATT_QT][2];
+        scores(sl, s);
+        float lmax[ATT_QT];
+        mask_max(s, min(ATT_KC, L), lmax);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (g4 * 8 + kt * 4 + i >= kvalid) s[tt][kt][i] = -INFINITY;
-      }
-      // this lane's max raw score per query tile
-      float lmax[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        lmax[tt] = fmaxf(fmaxf(fmaxf(s[tt][0][0], s[tt][0][1]), fmaxf(s[tt][0][2], s[tt][0][3])),
-                         fmaxf(fmaxf(s[tt][1][0], s[tt][1][1]), fmaxf(s[tt][1][2], s[tt][1][3])));
-      // Lazy rescaling: the reference max only moves when some score exceeds
-      // it by more than 2^LAZY_RESCALE (the previous chunk's PV is already in
-      // O), so P <= 2^LAZY_RESCALE and the common case needs no cross-lane
-      // reduction and leaves O alone.  An item's first chunk sets it.
-      const bool grow = (lmax[0] > thr[0]) | (lmax[1] > thr[1]);
-      if (fresh || __builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < ATT_QT; ++tt) {
           // the chunk's row max over the 4 lane groups of a query
-          const float cmax = xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2;
-          const float mnew = fresh ? cmax : fmaxf(mref[tt], cmax);
-          const float alpha = __builtin_amdgcn_exp2f(mref[tt] - mnew);
-          mref[tt] = mnew;
-          thr[tt] = (mnew + LAZY_RESCALE) * inv_scale_log2;
-          if (fresh) {  // the accumulators still hold the previous item's values
-            lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          mref[tt] = __builtin_ceilf(xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2);
+          thr[tt] = (mref[tt] + REF_HEADROOM) * inv_scale_log2;
+          lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          } else {
-            lsum[tt] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= alpha;
-          }
+          for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        fresh = false;
+        probs(s, mref, pprev);
+        pslot = sl;
+        ++p;
       }
-      // P = exp2(s*scale - mref), rounded to bf16, in the PV operand layout
+      // ---- further key chunks ----
+      for (int kc = 1; kc < nk; ++kc, ++p) {
+        stage_begin();
+        const int sl = p & (ATT_NST - 1);
+        f32x4 s[ATT_QT][2];
+        scores(sl, s);
+        __builtin_amdgcn_sched_barrier(0);
+        // V^T of the previous chunk, read while the S products run
+        bf16x8 vf[8];
+        read_vt(pslot, vf);
+        __builtin_amdgcn_sched_barrier(0);
+        float lmax[ATT_QT];
+        mask_max(s, min(ATT_KC, L - kc * ATT_KC), lmax);
+        bool over = false;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < ATT_QT; ++tt) over |= lmax[tt] > thr[tt];
+        if (__builtin_amdgcn_ballot_w64(over) != 0 && !flagged) {
+          flagged = true;
+          if (lane == 0) {
+            atomicOr(&ovf[uidx], 1ull << h);
+            atomicAdd(&table[0].y, 1);
+          }
+          ops += 2;
+        }
+        // P of this chunk and the previous chunk's PV product
+        bf16x8 pn[ATT_QT];
+        probs(s, mref, pn);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pprev[tt][kt * 4 + i] =
-                to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][kt][i], scale_log2, -mref[tt])));
-      pend = true;
-      pslot = slot;
-      if (comp.s == comp.ns - 1) {  // the item is done once this chunk's PV is in
-        fin = true;
-        fval0 = tval[0];
-        fval1 = tval[1];
-        fin_row = comp.row0 + comp.q0 + wave * 32;
-        fin_h = comp.h;
-        fin_n = comp.qn - wave * 32;
+          for (int tt = 0; tt < ATT_QT; ++tt)
+            oacc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev[tt], oacc[tt][dt], 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < ATT_QT; ++tt)
+          lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[tt], lsum[tt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < ATT_QT; ++tt) pprev[tt] = pn[tt];
+        pslot = sl;
+      }
+      // ---- the last chunk's PV product and the item's output ----
+      {
+        bf16x8 vf[8];
+        read_vt(pslot, vf);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int tt = 0; tt < ATT_QT; ++tt)
+            oacc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev[tt], oacc[tt][dt], 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < ATT_QT; ++tt)
+          lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[tt], lsum[tt], 0, 0, 0);
+        const int orow = row0 + q0 + wave * ATT_QW;
+#pragma unroll
+        for (int tt = 0; tt < ATT_QT; ++tt) {
+          if (tt * 16 >= nval) continue;  // wave-uniform
+          const float inv = 1.f / lsum[tt][0];
+          if (tt * 16 + l16 < nval) {
+            bf16* op = O + (size_t)(orow + tt * 16 + l16) * d + h * DH + g4 * 4;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+              bf16x4 o;
+              o[0] = to_bf16(oacc[tt][dt][0] * inv);
+              o[1] = to_bf16(oacc[tt][dt][1] * inv);
+              o[2] = to_bf16(oacc[tt][dt][2] * inv);
+              o[3] = to_bf16(oacc[tt][dt][3] * inv);
+              *(bf16x4*)(op + dt * 16) = o;
+            }
+          }
+          ops += 8;  // issued: lane l16 = 0 of a tile with rows is in range
+        }
       }
     }
-    cursor_next(comp, table, items, heads);
+    // next item (the compute cursor only moves item by item)
+    ++comp.r;
+    cursor_load(comp, table, items, heads);
   }
-  // the stream's last chunk
-  if (pend) pv_pending();
-  if (fin) store_fin();
+}
+
+// Exact attention for the items the kernel above flagged (a score more than
+// REF_HEADROOM doublings above the item's reference; never seen with logits
+// of ordinary size).  Two passes over the keys per query row: the row max,
+// then P with the rounding of the fast path (reference = ceil of the row max
+// in log2 units, P rounded to bf16, the sum taken over the rounded values) and
+// O = sum_j P_j V_j / sum_j P_j, rounded once to bf16.  Overwrites the rows the
+// fast kernel stored for those items.  One wave per query row; workgroups
+// stride over the units and return at once when nothing was flagged.
+constexpr int FB_WAVES = 4;
+
+__device__ __forceinline__ float fb_dot(const bf16* __restrict__ a, const bf16* __restrict__ b) {
+  float acc = 0.f;
+#pragma unroll 4
+  for (int t = 0; t < DH; t += 8) {
+    const bf16x8 x = *(const bf16x8*)(a + t);
+    const bf16x8 y = *(const bf16x8*)(b + t);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(to_f32(x[i]), to_f32(y[i]), acc);
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(FB_WAVES * 64) void block_attn_bf16_fallback_kernel(
+    const bf16* __restrict__ qkv, const int4* __restrict__ table,
+    const unsigned long long* __restrict__ ovf, int d, float scale_log2, bf16* __restrict__ O) {
+  if (table[0].y == 0) return;
+  __shared__ float pbuf[FB_WAVES][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int units = table[0].x;
+  const int ld = 3 * d;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    unsigned long long f = ovf[u];
+    const int4 e = table[1 + u];
+    const int row0 = e.x, L = e.y, q0 = e.z, qn = e.w;
+    while (f != 0) {
+      const int h = __ffsll((long long)f) - 1;
+      f &= f - 1;
+      const bf16* kbase = qkv + (size_t)row0 * ld + d + h * DH;
+      const bf16* vbase = qkv + (size_t)row0 * ld + 2 * d + h * DH;
+      for (int i = wave; i < qn; i += FB_WAVES) {
+        const bf16* q = qkv + (size_t)(row0 + q0 + i) * ld + h * DH;
+        float mx = -INFINITY;
+        for (int j = lane; j < L; j += 64) mx = fmaxf(mx, fb_dot(q, kbase + (size_t)j * ld));
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        const float mref = __builtin_ceilf(mx * scale_log2);
+        float o0 = 0.f, o1 = 0.f, psum = 0.f;  // this lane's dims 2*lane, 2*lane + 1
+        for (int j0 = 0; j0 < L; j0 += 64) {
+          const int j = j0 + lane;
+          float pj = 0.f;
+          if (j < L)
+            pj = to_f32(to_bf16(__builtin_amdgcn_exp2f(
+                __builtin_fmaf(fb_dot(q, kbase + (size_t)j * ld), scale_log2, -mref))));
+          psum += pj;
+          pbuf[wave][lane] = pj;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int jn = min(64, L - j0);
+          for (int t = 0; t < jn; ++t) {
+            const float pt = pbuf[wave][t];
+            const bf16* v = vbase + (size_t)(j0 + t) * ld + 2 * lane;
+            o0 = __builtin_fmaf(pt, to_f32(v[0]), o0);
+            o1 = __builtin_fmaf(pt, to_f32(v[1]), o1);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off);
+        const float inv = 1.f / psum;
+        bf16* op = O + (size_t)(row0 + q0 + i) * d + h * DH + 2 * lane;
+        op[0] = to_bf16(o0 * inv);
+        op[1] = to_bf16(o1 * inv);
+      }
+    }
+  }
 }
 
 static int g_num_cus = 0;
@@ -500,14 +634,25 @@ hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long lo
       n = 256;
     g_num_cus = n;
   }
-  build_unit_table_kernel<ATT_QG, ATT_QS, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(cu, S, B, (int4*)table);
+  // workspace: the unit table, then (256-byte aligned) one flag word per unit
+  unsigned long long* ovf =
+      (unsigned long long*)((char*)table + ((16 * (N + 1) + 255) / 256) * 256);
+  build_unit_table_kernel<ATT_QG, ATT_QS, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(cu, S, B, (int4*)table,
+                                                                                     ovf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long items = (long long)attn_unit_bound(N, S, B, ATT_QG) * heads;
+  const long long units = attn_unit_bound(N, S, B, ATT_QG);
+  const long long items = units * heads;
   const int grid = items < g_num_cus ? (int)items : g_num_cus;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
   hipLaunchKernelGGL(block_attn_bf16_kernel, dim3(grid), dim3(ATT_THREADS), 0, stream,
-                     (const bf16*)qkv, (const int4*)table, heads, d, scale_log2, (bf16*)o);
+                     (const bf16*)qkv, (int4*)table, ovf, heads, d, scale_log2, (bf16*)o);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int fgrid = units < 64 ? (int)units : 64;
+  hipLaunchKernelGGL(block_attn_bf16_fallback_kernel, dim3(fgrid), dim3(FB_WAVES * 64), 0, stream,
+                     (const bf16*)qkv, (const int4*)table, (const unsigned long long*)ovf, d, scale_log2,
+                     (bf16*)o);
   return hipGetLastError();
 }
 

@@ -70,19 +70,22 @@ __device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnU
 }
 
 // Unit table for kernels that read their units with scalar loads.
-// table[0].x = number of units; table[1 + i] = {row0, L, q0, qn} of the i-th
+// table[0] = {number of units, 0, 0, 0} (.y counts flagged items afterwards);
+// table[1 + i] = {row0, L, q0, qn} of the i-th
 // unit in order of decreasing cost, the cost being the number of ring stages
 // a unit takes, ceil(qn/QS) + ceil(L/KC) (capped at 1023; the order of units
 // of equal cost is unspecified).  With the costliest units first, a
 // persistent kernel that deals them out in a snake order (round r hands
 // position r*G + w to workgroup w for even r, to G-1-w for odd r) keeps its
 // workgroups within about one unit of each other.
-// Every unit holds at least one row, so N + 1 entries always suffice.
+// Every unit holds at least one row, so N + 1 entries always suffice.  If
+// `flags` is not null, flags[i] is cleared for every unit i.
 // One workgroup; a counting sort over the cost: a histogram pass and a
 // placement pass over the sequences, 1024 sequences at a time.
 template <int QG, int QS, int KC>
 __global__ __launch_bounds__(1024) void build_unit_table_kernel(const int* __restrict__ cu, int S,
-                                                               int B, int4* __restrict__ table) {
+                                                               int B, int4* __restrict__ table,
+                                                               unsigned long long* __restrict__ flags) {
   constexpr int BINS = 1024;
   __shared__ int next[BINS];  // per cost bin: count, then next free position
   __shared__ int scan[BINS];
@@ -114,7 +117,10 @@ __global__ __launch_bounds__(1024) void build_unit_table_kernel(const int* __res
         for (int v = 0; v < n; ++v) {
           const int4 e = unit(start, len, v);
           const int pos = atomicAdd(&next[bin_of(e)], 1);
-          if (pass == 1) table[1 + pos] = e;
+          if (pass == 1) {
+            table[1 + pos] = e;
+            if (flags) flags[pos] = 0;
+          }
         }
       }
     }

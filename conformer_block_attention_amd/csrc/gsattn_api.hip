@@ -153,8 +153,9 @@ const char* gs_last_error_detail(void) { return g_detail; }
 
 size_t gs_block_attn_workspace_bytes(int64_t total_frames) {
   if (total_frames < 0) return 0;
-  // work-unit table: a count and at most one 16-byte entry per row
-  return align_up(16 * ((size_t)total_frames + 1));
+  // work-unit table: a header and at most one 16-byte entry per row; then one
+  // 8-byte word per unit flagging heads for the exact fallback
+  return align_up(16 * ((size_t)total_frames + 1)) + align_up(8 * ((size_t)total_frames + 1));
 }
 
 size_t gs_block_mhsa_workspace_bytes(int64_t total_frames, int32_t d_model, gs_dtype dtype) {

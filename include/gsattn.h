@@ -114,8 +114,11 @@ size_t gs_block_attn_workspace_bytes(int64_t total_frames);
  * Step 2 alone: o[N][d] from qkv[N][3d] (layout as produced by gs_qkv_proj):
  * per block and head, softmax(Q K^T / sqrt(dh)) V, keys limited to the block.
  *   workspace  device scratch of >= gs_block_attn_workspace_bytes(N) bytes,
- *              256-byte aligned (the table of work units built from cu_seqlens);
- *              calls that share a workspace must not overlap in time.
+ *              256-byte aligned (the table of work units built from cu_seqlens
+ *              and, for bf16, one word per unit marking the heads whose logits
+ *              ran so far above those of the unit's first 32 keys that they go
+ *              to an exact two-pass recomputation); calls that share a
+ *              workspace must not overlap in time.
  */
 gs_status gs_block_attn(const void* qkv, const int32_t* cu_seqlens, int32_t num_seqs,
                         int64_t total_frames, int32_t d_model, int32_t heads,

@@ -43,10 +43,12 @@ def test_version_and_status_strings(lib):
 def test_workspace_bytes(lib):
     n, d = 1000, 1024
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    assert lib.gs_block_attn_workspace_bytes(n) == al(16 * (n + 1))
+    # unit table (16 B per unit) and a flag word per unit, units <= n + 1
+    attn = al(16 * (n + 1)) + al(8 * (n + 1))
+    assert lib.gs_block_attn_workspace_bytes(n) == attn
     for dt, e in ((gsattn.GS_BF16, 2), (gsattn.GS_F32, 4)):
         got = lib.gs_block_mhsa_workspace_bytes(n, d, dt)
-        assert got == al(n * 3 * d * e) + al(n * d * e) + al(16 * (n + 1)) + 256
+        assert got == al(n * 3 * d * e) + al(n * d * e) + attn + 256
     assert lib.gs_block_mhsa_workspace_bytes(-1, d, gsattn.GS_BF16) == 0
     assert lib.gs_block_mhsa_workspace_bytes(n, d, 7) == 0
 

@@ -110,6 +110,49 @@ def test_stage_block_attn(orc, dtype, lengths, B):
     assert worst <= 1.0, worst
 
 
+def test_stage_block_attn_large_logits(orc):
+    """Logits far above those of an item's first key chunk.  The bf16 kernel fixes
+    a per-row reference at the first chunk and hands an item to its exact
+    two-pass fallback once a later score exceeds it by more than 64 doublings
+    (raw score > 64 / log2(e) * sqrt(128) = 502 here); below that the large
+    weights stay inside the fast path.
+      block 0, head 0: keys 0..31 zero, key 100 and all queries = 7 (score 554):
+                        every row goes to the fallback
+      block 0, head 1: keys 0..31 zero, key 195 (partial last chunk) = 7 and
+                        queries = 7: fallback, decided in the masked chunk
+      block 1, head 1: keys 0..31 zero, key 50 and queries = 6 (score 407):
+                        fast path with weights up to 2^52
+    Everything else is N(0, 1)."""
+    G.print_case("stage_block_attn_large_logits")
+    d, H, B = 256, 2, 200
+    lengths = [200, 130, 90]
+    n = int(np.sum(lengths))
+    g = torch.Generator().manual_seed(9)
+    qkv = torch.randn(n, 3 * d, generator=g)
+    q = lambda r, h: (r, slice(h * 128, (h + 1) * 128))
+    k = lambda r, h: (r, slice(d + h * 128, d + (h + 1) * 128))
+    qkv[k(slice(0, 32), 0)] = 0.0
+    qkv[k(100, 0)] = 7.0
+    qkv[q(slice(0, 200), 0)] = 7.0
+    qkv[k(slice(0, 32), 1)] = 0.0
+    qkv[k(195, 1)] = 7.0
+    qkv[q(slice(0, 200), 1)] = 7.0
+    qkv[k(slice(200, 232), 1)] = 0.0
+    qkv[k(250, 1)] = 6.0
+    qkv[q(slice(200, 330), 1)] = 6.0
+    qkv_cpu = qkv.to(torch.bfloat16)
+    cu = workloads.cu_seqlens(lengths)
+    o = gsattn.block_attn(qkv_cpu.to(G.dev()), torch.from_numpy(cu).to(G.dev()), H, B)
+    torch.cuda.synchronize()
+    ref = orc.block_attn(qkv_cpu, cu, H, B)
+    got = o.double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    bound = _attn_bound(qkv_cpu.double().numpy(), cu, H, B, ref, torch.bfloat16)
+    worst = float(np.max(np.abs(got - ref) / bound))
+    print(f"  worst error / bound = {worst:.3f}", flush=True)
+    assert worst <= 1.0, worst
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_stage_out_proj(orc, dtype):
     G.print_case("stage_out_proj", dtype=dtype)
