@@ -39,21 +39,20 @@
 
 namespace gs {
 
-#ifndef ATT_WAVES_CFG
-#define ATT_WAVES_CFG 8
-#endif
-constexpr int ATT_WAVES = ATT_WAVES_CFG;
+constexpr int ATT_WAVES = 8;         // 7 math waves and one copy wave
+constexpr int ATT_PRODUCER = ATT_WAVES - 1;
 constexpr int ATT_THREADS = ATT_WAVES * 64;
-constexpr int ATT_QT = 16 / ATT_WAVES;  // 16-row query tiles per wave
-constexpr int ATT_QW = 16 * ATT_QT;  // query rows per wave
-constexpr int ATT_QG = ATT_WAVES * ATT_QW;  // query rows per unit (4 waves x 64)
+constexpr int ATT_QT = 2;            // 16-row query tiles per math wave
+constexpr int ATT_QW = 16 * ATT_QT;  // query rows per math wave
+constexpr int ATT_QG = ATT_PRODUCER * ATT_QW;  // query rows per unit (7 waves x 32)
 constexpr int ATT_QS = 64;           // query rows per query stage
-constexpr int ATT_WPQ = ATT_QS / ATT_QW;  // waves served by one query stage
+constexpr int ATT_WPQ = ATT_QS / ATT_QW;  // math waves served by one query stage
 constexpr int ATT_KC = 32;           // keys per key chunk
 constexpr int DH = 128;
 constexpr int ATT_NST = 8;           // ring stages
+constexpr int ATT_AHEAD = 4;         // copies run this many stages ahead (<= 63 in flight)
 constexpr int STAGE_ELEMS = 8192;    // 16 KB: 64 rows of 128 bf16
-constexpr int COPIES = 16 / ATT_WAVES;  // 1 KB wave copies per wave per stage
+constexpr int COPIES = 16;           // 1 KB wave copies per stage, all by the copy wave
 
 // LDS rows are 128 bf16 = 256 B = 16 chunks of 16 B, one full window of the
 // 64 four-byte banks; chunk c of row r is stored at physical chunk c ^ swz(r)
@@ -183,18 +182,42 @@ __device__ __forceinline__ void stream_barrier() {
 }
 
 // Wait until at most n of this wave's vector-memory operations are pending
-// (n rounded down to even and capped at 30, which only waits longer).
+// (n rounded down to even and capped at 62, which only waits longer).
 #define GS_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
-  switch (n >= 30 ? 15 : (n < 0 ? 0 : n >> 1)) {
-    case 0: GS_VMCNT(0); break;    case 1: GS_VMCNT(2); break;
-    case 2: GS_VMCNT(4); break;    case 3: GS_VMCNT(6); break;
-    case 4: GS_VMCNT(8); break;    case 5: GS_VMCNT(10); break;
-    case 6: GS_VMCNT(12); break;   case 7: GS_VMCNT(14); break;
-    case 8: GS_VMCNT(16); break;   case 9: GS_VMCNT(18); break;
-    case 10: GS_VMCNT(20); break;  case 11: GS_VMCNT(22); break;
-    case 12: GS_VMCNT(24); break;  case 13: GS_VMCNT(26); break;
-    case 14: GS_VMCNT(28); break;  default: GS_VMCNT(30); break;
+  switch (n >= 62 ? 31 : (n < 0 ? 0 : n >> 1)) {
+    case 0: GS_VMCNT(0); break;
+    case 1: GS_VMCNT(2); break;
+    case 2: GS_VMCNT(4); break;
+    case 3: GS_VMCNT(6); break;
+    case 4: GS_VMCNT(8); break;
+    case 5: GS_VMCNT(10); break;
+    case 6: GS_VMCNT(12); break;
+    case 7: GS_VMCNT(14); break;
+    case 8: GS_VMCNT(16); break;
+    case 9: GS_VMCNT(18); break;
+    case 10: GS_VMCNT(20); break;
+    case 11: GS_VMCNT(22); break;
+    case 12: GS_VMCNT(24); break;
+    case 13: GS_VMCNT(26); break;
+    case 14: GS_VMCNT(28); break;
+    case 15: GS_VMCNT(30); break;
+    case 16: GS_VMCNT(32); break;
+    case 17: GS_VMCNT(34); break;
+    case 18: GS_VMCNT(36); break;
+    case 19: GS_VMCNT(38); break;
+    case 20: GS_VMCNT(40); break;
+    case 21: GS_VMCNT(42); break;
+    case 22: GS_VMCNT(44); break;
+    case 23: GS_VMCNT(46); break;
+    case 24: GS_VMCNT(48); break;
+    case 25: GS_VMCNT(50); break;
+    case 26: GS_VMCNT(52); break;
+    case 27: GS_VMCNT(54); break;
+    case 28: GS_VMCNT(56); break;
+    case 29: GS_VMCNT(58); break;
+    case 30: GS_VMCNT(60); break;
+    default: GS_VMCNT(62); break;
   }
 }
 #undef GS_VMCNT
@@ -253,10 +276,10 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < ATT_NST - 1; ++i) mark[i] = 0;
 
-  // ---- copies of one stage into ring slot `slot` --------------------------
-  // 16 KB = 16 wave copies of 1 KB (4 rows of 256 B); wave w does copies
-  // w, w+4, w+8, w+12; lane -> row r0 + lane/16, physical chunk lane%16.  In a
-  // key stage rows 0..31 are the chunk's K rows and rows 32..63 its V rows.
+  // ---- copies of one stage into ring slot `slot` (the copy wave) ----------
+  // 16 KB = 16 wave copies of 1 KB (4 rows of 256 B); lane -> row r0 +
+  // lane/16, physical chunk lane%16.  In a key stage rows 0..31 are the
+  // chunk's K rows and rows 32..63 its V rows.
   auto issue = [&](const Cursor& c, int slot) __attribute__((always_inline)) {
     GS_LDS bf16* dst = (GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
     const int pc = lane & 15;
@@ -265,7 +288,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
       const int qlast = c.q0 + c.qn - 1;
 #pragma unroll
       for (int j = 0; j < COPIES; ++j) {
-        const int r0 = (j * ATT_WAVES + wave) * 4;
+        const int r0 = j * 4;
         const int rr = r0 + (lane >> 4);
         int q = q0 + rr;
         q = q <= qlast ? q : qlast;
@@ -276,7 +299,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
       const int k0 = (c.s - c.nq) * ATT_KC;
 #pragma unroll
       for (int j = 0; j < COPIES; ++j) {
-        const int r0 = (j * ATT_WAVES + wave) * 4;
+        const int r0 = j * 4;
         const bool isv = r0 >= ATT_KC;
         const int kr = (r0 + (lane >> 4)) & (ATT_KC - 1);
         int key = k0 + kr;
@@ -290,21 +313,39 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   };
 
   // ---- stream -------------------------------------------------------------------
-  // Copies run AHEAD = NST-2 stages ahead: the slot of the previous stage stays
-  // resident for one more iteration, because its PV product is done then.
-  constexpr int AHEAD = ATT_NST - 2;
+  // The copy wave runs AHEAD stages ahead of the math waves; at the start of
+  // stage p it has waited for stage p's copies and then refills the slot of
+  // stage p - (NST - AHEAD) (the math waves read the slots of p and p-1).
+  constexpr int AHEAD = ATT_AHEAD;
+  const bool producer = wave == ATT_PRODUCER;
   Cursor comp, iss;
   comp.r = 0;
   cursor_load(comp, table, items, heads);
   if (!comp.valid) return;  // uniform over the workgroup
-  iss = comp;
+  if (producer) {
+    // ---- the copy wave: one barrier per stream position, like the math waves
+    iss = comp;
 #pragma unroll
-  for (int s = 0; s < AHEAD; ++s) {
-    if (iss.valid) {
-      issue(iss, s);
-      cursor_next(iss, table, items, heads);
+    for (int s = 0; s < AHEAD; ++s) {
+      if (iss.valid) {
+        issue(iss, s);
+        cursor_next(iss, table, items, heads);
+      }
+      mark[s] = ops;
     }
-    mark[s] = ops;
+    for (int p = 0; comp.valid; ++p) {
+      wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - mark[0]));  // stage p has landed
+      stream_barrier();  // ... for everyone; everyone is done with stage p-2
+      if (iss.valid) {
+        issue(iss, (p + AHEAD) & (ATT_NST - 1));
+        cursor_next(iss, table, items, heads);
+      }
+#pragma unroll
+      for (int i = 0; i < AHEAD - 1; ++i) mark[i] = mark[i + 1];
+      mark[AHEAD - 1] = ops;  // position p+AHEAD (if issued; otherwise never waited for)
+      cursor_next(comp, table, items, heads);
+    }
+    return;  // every copy it issued has landed
   }
 
   // ---- per-wave query state: rows ATT_QW*wave + 16*tt + lane%16 of the item ----
@@ -338,19 +379,10 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   const unsigned ring_base = (unsigned)(uintptr_t)(GS_LDS bf16*)ring;
   constexpr unsigned STAGE_BYTES = STAGE_ELEMS * 2;
 
-  // Start of stream position p: wait for its copies, meet the other waves, and
-  // refill the slot of position p-2 with position p+AHEAD.
+  // Start of stream position p (the copy wave has waited for its copies).
   int p = 0;
   auto stage_begin = [&]() __attribute__((always_inline)) {
-    wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - mark[0]));
-    stream_barrier();  // everyone's landed; everyone is done with stage p-2
-    if (iss.valid) {
-      issue(iss, (p + AHEAD) & (ATT_NST - 1));
-      cursor_next(iss, table, items, heads);
-    }
-#pragma unroll
-    for (int i = 0; i < AHEAD - 1; ++i) mark[i] = mark[i + 1];
-    mark[AHEAD - 1] = ops;  // position p+AHEAD (if issued; otherwise never waited for)
+    stream_barrier();  // stage p has landed; everyone is done with stage p-2
   };
 
   // V^T fragments of the chunk in ring slot `sl` (16 dh x 32 keys per dh tile).
@@ -637,7 +669,7 @@ hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long lo
   // workspace: the unit table, then (256-byte aligned) one flag word per unit
   unsigned long long* ovf =
       (unsigned long long*)((char*)table + ((16 * (N + 1) + 255) / 256) * 256);
-  build_unit_table_kernel<ATT_QG, ATT_QS, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(cu, S, B, (int4*)table,
+  build_unit_table_kernel<ATT_QG, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(cu, S, B, (int4*)table,
                                                                                      ovf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -72,9 +72,9 @@ __device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnU
 // Unit table for kernels that read their units with scalar loads.
 // table[0] = {number of units, 0, 0, 0} (.y counts flagged items afterwards);
 // table[1 + i] = {row0, L, q0, qn} of the i-th
-// unit in order of decreasing cost, the cost being the number of ring stages
-// a unit takes, ceil(qn/QS) + ceil(L/KC) (capped at 1023; the order of units
-// of equal cost is unspecified).  With the costliest units first, a
+// unit in order of decreasing cost, the cost being the number of key chunks
+// of KC keys a unit takes, ceil(L/KC) (capped at 1023; the order of units of
+// equal cost is unspecified).  With the costliest units first, a
 // persistent kernel that deals them out in a snake order (round r hands
 // position r*G + w to workgroup w for even r, to G-1-w for odd r) keeps its
 // workgroups within about one unit of each other.
@@ -82,7 +82,7 @@ __device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnU
 // `flags` is not null, flags[i] is cleared for every unit i.
 // One workgroup; a counting sort over the cost: a histogram pass and a
 // placement pass over the sequences, 1024 sequences at a time.
-template <int QG, int QS, int KC>
+template <int QG, int KC>
 __global__ __launch_bounds__(1024) void build_unit_table_kernel(const int* __restrict__ cu, int S,
                                                                int B, int4* __restrict__ table,
                                                                unsigned long long* __restrict__ flags) {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(1024) void build_unit_table_kernel(const int* __res
     return make_int4(start + j * B, L, g * QG, min(QG, L - g * QG));
   };
   auto bin_of = [&](int4 e) {  // bin 0 holds the costliest units
-    const int cost = (e.w + QS - 1) / QS + (e.y + KC - 1) / KC;
+    const int cost = (e.y + KC - 1) / KC;
     return BINS - 1 - min(cost, BINS - 1);
   };
   for (int pass = 0; pass < 2; ++pass) {
