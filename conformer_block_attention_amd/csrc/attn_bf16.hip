@@ -280,9 +280,14 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   // 16 KB = 16 wave copies of 1 KB (4 rows of 256 B); lane -> row r0 +
   // lane/16, physical chunk lane%16.  In a key stage rows 0..31 are the
   // chunk's K rows and rows 32..63 its V rows.
+  // Addresses are a workgroup-uniform base (the block's first row in the
+  // part and head being copied) plus a 32-bit byte offset per lane, the form
+  // the copy instruction takes with the base in SGPRs (cheaper to issue than
+  // a 64-bit address per lane).
   auto issue = [&](const Cursor& c, int slot) __attribute__((always_inline)) {
     GS_LDS bf16* dst = (GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
     const int pc = lane & 15;
+    const char* blk = (const char*)(qkv + (size_t)c.row0 * ld + c.h * DH);
     if (c.s < c.nq) {  // query stage: 64 rows
       const int q0 = c.q0 + c.s * ATT_QS;
       const int qlast = c.q0 + c.qn - 1;
@@ -293,10 +298,12 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         int q = q0 + rr;
         q = q <= qlast ? q : qlast;
         const int lc = pc ^ swz_q(rr);
-        copy16_to_lds(qkv + (size_t)(c.row0 + q) * ld + c.h * DH + lc * 8, dst + r0 * DH);
+        copy16_to_lds(blk + (unsigned)(q * ld + lc * 8) * 2u, dst + r0 * DH);
       }
     } else {           // key chunk: 32 K rows then 32 V rows
       const int k0 = (c.s - c.nq) * ATT_KC;
+      const char* kb = blk + (size_t)d * 2;
+      const char* vb = blk + (size_t)d * 4;
 #pragma unroll
       for (int j = 0; j < COPIES; ++j) {
         const int r0 = j * 4;
@@ -305,8 +312,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         int key = k0 + kr;
         key = key < c.L ? key : c.L - 1;
         const int lc = pc ^ (isv ? swz_v(kr) : swz_k(kr));
-        copy16_to_lds(qkv + (size_t)(c.row0 + key) * ld + (isv ? 2 * d : d) + c.h * DH + lc * 8,
-                      dst + r0 * DH);
+        copy16_to_lds((isv ? vb : kb) + (unsigned)(key * ld + lc * 8) * 2u, dst + r0 * DH);
       }
     }
     ops += COPIES;
