@@ -45,8 +45,6 @@ constexpr int ATT_THREADS = ATT_WAVES * 64;
 constexpr int ATT_QT = 2;            // 16-row query tiles per math wave
 constexpr int ATT_QW = 16 * ATT_QT;  // query rows per math wave
 constexpr int ATT_QG = ATT_PRODUCER * ATT_QW;  // query rows per unit (7 waves x 32)
-constexpr int ATT_QS = 64;           // query rows per query stage
-constexpr int ATT_WPQ = ATT_QS / ATT_QW;  // math waves served by one query stage
 constexpr int ATT_KC = 32;           // keys per key chunk
 constexpr int DH = 128;
 constexpr int ATT_NST = 8;           // ring stages
@@ -230,8 +228,8 @@ struct Cursor {
   int v;       // work item (unit position * heads + head)
   bool valid;  // false past the workgroup's last item
   int row0, L, q0, qn, h;
-  int s;       // stage index inside the item
-  int nq, ns;  // query stages, all stages
+  int s;       // key chunk inside the item
+  int ns;      // key chunks of the item
 };
 
 __device__ __forceinline__ void cursor_load(Cursor& c, const int4* __restrict__ table, int items,
@@ -244,8 +242,7 @@ __device__ __forceinline__ void cursor_load(Cursor& c, const int4* __restrict__ 
     const int4 e = table[1 + u];  // wave-uniform address: scalar load
     c.h = c.v - u * heads;
     c.row0 = e.x; c.L = e.y; c.q0 = e.z; c.qn = e.w;
-    c.nq = (c.qn + ATT_QS - 1) / ATT_QS;
-    c.ns = c.nq + (c.L + ATT_KC - 1) / ATT_KC;
+    c.ns = (c.L + ATT_KC - 1) / ATT_KC;
   }
 }
 
@@ -288,20 +285,8 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     GS_LDS bf16* dst = (GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
     const int pc = lane & 15;
     const char* blk = (const char*)(qkv + (size_t)c.row0 * ld + c.h * DH);
-    if (c.s < c.nq) {  // query stage: 64 rows
-      const int q0 = c.q0 + c.s * ATT_QS;
-      const int qlast = c.q0 + c.qn - 1;
-#pragma unroll
-      for (int j = 0; j < COPIES; ++j) {
-        const int r0 = j * 4;
-        const int rr = r0 + (lane >> 4);
-        int q = q0 + rr;
-        q = q <= qlast ? q : qlast;
-        const int lc = pc ^ swz_q(rr);
-        copy16_to_lds(blk + (unsigned)(q * ld + lc * 8) * 2u, dst + r0 * DH);
-      }
-    } else {           // key chunk: 32 K rows then 32 V rows
-      const int k0 = (c.s - c.nq) * ATT_KC;
+    {  // key chunk: 32 K rows then 32 V rows
+      const int k0 = c.s * ATT_KC;
       const char* kb = blk + (size_t)d * 2;
       const char* vb = blk + (size_t)d * 4;
 #pragma unroll
@@ -353,6 +338,26 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     }
     return;  // every copy it issued has landed
   }
+
+  // ---- query rows: a math wave loads the fragments of its rows of the next
+  // item straight from global memory while the current item runs ----
+  bf16x8 qnext[ATT_QT][4];
+  int qmark = 0;  // its loads are complete once at most ops - qmark are pending
+  auto load_q = [&](const Cursor& c) __attribute__((always_inline)) {
+    if (wave * ATT_QW >= c.qn) return;  // no rows for this wave
+    const int qlast = c.qn - 1;
+    const bf16* blk = qkv + (size_t)(c.row0 + c.q0) * ld + c.h * DH + g4 * 8;
+#pragma unroll
+    for (int tt = 0; tt < ATT_QT; ++tt) {
+      int r = wave * ATT_QW + tt * 16 + l16;
+      r = r <= qlast ? r : qlast;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) qnext[tt][kc] = *(const bf16x8*)(blk + (size_t)r * ld + kc * 32);
+    }
+    ops += 4 * ATT_QT;
+    qmark = ops;
+  };
+  load_q(comp);
 
   // ---- per-wave query state: rows ATT_QW*wave + 16*tt + lane%16 of the item ----
   bf16x8 qf[ATT_QT][4];
@@ -444,27 +449,22 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
 
   // ---- items ----
   for (; comp.valid; ) {
-    const int nq = comp.nq;
-    const int nk = comp.ns - comp.nq;
+    const int nk = comp.ns;
     const int nval = min(ATT_QW, comp.qn - wave * ATT_QW);  // this wave's query rows
     const int row0 = comp.row0, L = comp.L, q0 = comp.q0, h = comp.h;
     const int uidx = comp.v / heads;  // the unit's position in the table
-    // ---- query stages: wave w loads its rows at stage w / ATT_WPQ ----
-    for (int qs = 0; qs < nq; ++qs, ++p) {
-      stage_begin();
-      if (wave / ATT_WPQ == qs) {
-        const GS_LDS bf16* st = (const GS_LDS bf16*)&ring[(p & (ATT_NST - 1)) * STAGE_ELEMS];
+    // ---- this wave's query fragments, and the loads of the next item's ----
+    Cursor nxt;
+    nxt.r = comp.r + 1;
+    cursor_load(nxt, table, items, heads);
+    if (nval > 0) {
+      wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - qmark));
 #pragma unroll
-        for (int tt = 0; tt < ATT_QT; ++tt) {
-          const int rr = (wave % ATT_WPQ) * ATT_QW + tt * 16 + l16;
+      for (int tt = 0; tt < ATT_QT; ++tt)
 #pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            const int lc = kc * 4 + g4;
-            qf[tt][kc] = *(const GS_LDS bf16x8*)(st + rr * DH + (lc ^ swz_q(rr)) * 8);
-          }
-        }
-      }
+        for (int kc = 0; kc < 4; ++kc) qf[tt][kc] = qnext[tt][kc];
     }
+    if (nxt.valid) load_q(nxt);
     if (nval <= 0) {  // no rows for this wave: only keep the stream going
       for (int kc = 0; kc < nk; ++kc, ++p) stage_begin();
     } else {
@@ -574,9 +574,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         }
       }
     }
-    // next item (the compute cursor only moves item by item)
-    ++comp.r;
-    cursor_load(comp, table, items, heads);
+    comp = nxt;  // (the compute cursor only moves item by item)
   }
 }
 
