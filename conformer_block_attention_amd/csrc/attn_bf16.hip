@@ -281,14 +281,35 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   // part and head being copied) plus a 32-bit byte offset per lane, the form
   // the copy instruction takes with the base in SGPRs (cheaper to issue than
   // a 64-bit address per lane).
+  // Lane byte offsets of the 16 copies of a chunk relative to its first K
+  // (copies 0..7) or V (copies 8..15) row, for chunks wholly inside the
+  // block: the same for every chunk (set up by the copy wave only).
+  unsigned koff_c[COPIES / 2], voff_c[COPIES / 2];
   auto issue = [&](const Cursor& c, int slot) __attribute__((always_inline)) {
     GS_LDS bf16* dst = (GS_LDS bf16*)&ring[slot * STAGE_ELEMS];
-    const int pc = lane & 15;
-    const char* blk = (const char*)(qkv + (size_t)c.row0 * ld + c.h * DH);
-    {  // key chunk: 32 K rows then 32 V rows
-      const int k0 = c.s * ATT_KC;
-      const char* kb = blk + (size_t)d * 2;
-      const char* vb = blk + (size_t)d * 4;
+    const int k0 = __builtin_amdgcn_readfirstlane(c.s * ATT_KC);
+    const int brow = __builtin_amdgcn_readfirstlane(c.row0);
+    const int hcol = __builtin_amdgcn_readfirstlane(c.h * DH);
+    const char* kb = (const char*)(qkv + (size_t)brow * ld + d + hcol);
+    const char* vb = kb + (size_t)d * 2;
+    if (k0 + ATT_KC <= c.L) {  // a full chunk: uniform base + fixed lane offsets
+      const size_t c0 = (size_t)k0 * ld * 2;
+      // (the empty asm keeps each offset a 32-bit value at its use, so the copy
+      // takes the SGPR-base form)
+#pragma unroll
+      for (int j = 0; j < COPIES / 2; ++j) {
+        unsigned o = koff_c[j];
+        asm volatile("" : "+v"(o));
+        copy16_to_lds(kb + c0 + o, dst + j * 4 * DH);
+      }
+#pragma unroll
+      for (int j = 0; j < COPIES / 2; ++j) {
+        unsigned o = voff_c[j];
+        asm volatile("" : "+v"(o));
+        copy16_to_lds(vb + c0 + o, dst + (ATT_KC + j * 4) * DH);
+      }
+    } else {  // the block's partial last chunk: keys past its end repeat its last row
+      const int pc = lane & 15;
 #pragma unroll
       for (int j = 0; j < COPIES; ++j) {
         const int r0 = j * 4;
@@ -315,6 +336,12 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   if (!comp.valid) return;  // uniform over the workgroup
   if (producer) {
     // ---- the copy wave: one barrier per stream position, like the math waves
+#pragma unroll
+    for (int j = 0; j < COPIES / 2; ++j) {
+      const int kr = j * 4 + (lane >> 4);
+      koff_c[j] = (unsigned)(kr * ld + ((lane & 15) ^ swz_k(kr)) * 8) * 2u;
+      voff_c[j] = (unsigned)(kr * ld + ((lane & 15) ^ swz_v(kr)) * 8) * 2u;
+    }
     iss = comp;
 #pragma unroll
     for (int s = 0; s < AHEAD; ++s) {
