@@ -254,12 +254,83 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int4* __restrict__ 
   }
 }
 
+// Exact attention for one item (unit u of the table, head h) whose scores ran
+// more than REF_HEADROOM doublings above its reference (never seen with
+// logits of ordinary size).  Two passes over the keys per query row: the row
+// max, then P with the rounding of the fast path (reference = ceil of the row
+// max in log2 units, P rounded to bf16, the sum taken over the rounded values)
+// and O = sum_j P_j V_j / sum_j P_j, rounded once to bf16.  Waves w0, w0 +
+// nw, ... of the calling waves take one query row each; pbuf holds 64 floats
+// per calling wave.
+__device__ __forceinline__ float exact_dot(const bf16* __restrict__ a, const bf16* __restrict__ b) {
+  float acc = 0.f;
+#pragma unroll 4
+  for (int t = 0; t < DH; t += 8) {
+    const bf16x8 x = *(const bf16x8*)(a + t);
+    const bf16x8 y = *(const bf16x8*)(b + t);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(to_f32(x[i]), to_f32(y[i]), acc);
+  }
+  return acc;
+}
+
+__device__ void exact_item(const bf16* __restrict__ qkv, int4 e, int h, int d, float scale_log2,
+                           bf16* __restrict__ O, int w0, int nw, float* pbuf) {
+  const int lane = threadIdx.x & 63;
+  const int ld = 3 * d;
+  const int row0 = e.x, L = e.y, q0 = e.z, qn = e.w;
+  const bf16* kbase = qkv + (size_t)row0 * ld + d + h * DH;
+  const bf16* vbase = qkv + (size_t)row0 * ld + 2 * d + h * DH;
+  for (int i = w0; i < qn; i += nw) {
+    const bf16* q = qkv + (size_t)(row0 + q0 + i) * ld + h * DH;
+    float mx = -INFINITY;
+    for (int j = lane; j < L; j += 64) mx = fmaxf(mx, exact_dot(q, kbase + (size_t)j * ld));
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mref = __builtin_ceilf(mx * scale_log2);
+    float o0 = 0.f, o1 = 0.f, psum = 0.f;  // this lane's dims 2*lane, 2*lane + 1
+    for (int j0 = 0; j0 < L; j0 += 64) {
+      const int j = j0 + lane;
+      float pj = 0.f;
+      if (j < L)
+        pj = to_f32(to_bf16(__builtin_amdgcn_exp2f(
+            __builtin_fmaf(exact_dot(q, kbase + (size_t)j * ld), scale_log2, -mref))));
+      psum += pj;
+      pbuf[lane] = pj;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int jn = min(64, L - j0);
+      for (int t = 0; t < jn; ++t) {
+        const float pt = pbuf[t];
+        const bf16* v = vbase + (size_t)(j0 + t) * ld + 2 * lane;
+        o0 = __builtin_fmaf(pt, to_f32(v[0]), o0);
+        o1 = __builtin_fmaf(pt, to_f32(v[1]), o1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off);
+    const float inv = 1.f / psum;
+    bf16* op = O + (size_t)(row0 + q0 + i) * d + h * DH + 2 * lane;
+    op[0] = to_bf16(o0 * inv);
+    op[1] = to_bf16(o1 * inv);
+  }
+}
+
+// Items a workgroup flagged are listed in LDS (up to this many; beyond that
+// every item of the workgroup is checked against the flag words).
+constexpr int ATT_FLIST = 64;
+
 __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     const bf16* __restrict__ qkv, int4* __restrict__ table, unsigned long long* __restrict__ ovf,
     int heads, int d, float scale_log2, bf16* __restrict__ O) {
   __shared__ __attribute__((aligned(1024))) bf16 ring[ATT_NST * STAGE_ELEMS];
+  __shared__ int flist[1 + ATT_FLIST];          // count, then flagged item ids
+  __shared__ float pbuf[ATT_PRODUCER][64];      // the exact path's P, per math wave
 
   const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) flist[0] = 0;  // (ordered before any use by the first barrier)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ld = 3 * d;
   const int g4 = lane >> 4;   // lane group
@@ -363,7 +434,8 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
       mark[AHEAD - 1] = ops;  // position p+AHEAD (if issued; otherwise never waited for)
       cursor_next(comp, table, items, heads);
     }
-    return;  // every copy it issued has landed
+    stream_barrier();  // the math waves' closing barrier (every copy it issued has landed)
+    return;
   }
 
   // ---- query rows: a math wave loads the fragments of its rows of the next
@@ -548,9 +620,10 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           flagged = true;
           if (lane == 0) {
             atomicOr(&ovf[uidx], 1ull << h);
-            atomicAdd(&table[0].y, 1);
+            const int pos = atomicAdd(&flist[0], 1);
+            if (pos < ATT_FLIST) flist[1 + pos] = comp.v;
           }
-          ops += 2;
+          ops += 1;
         }
         // P of this chunk and the previous chunk's PV product
         bf16x8 pn[ATT_QT];
@@ -603,83 +676,24 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     }
     comp = nxt;  // (the compute cursor only moves item by item)
   }
-}
-
-// Exact attention for the items the kernel above flagged (a score more than
-// REF_HEADROOM doublings above the item's reference; never seen with logits
-// of ordinary size).  Two passes over the keys per query row: the row max,
-// then P with the rounding of the fast path (reference = ceil of the row max
-// in log2 units, P rounded to bf16, the sum taken over the rounded values) and
-// O = sum_j P_j V_j / sum_j P_j, rounded once to bf16.  Overwrites the rows the
-// fast kernel stored for those items.  One wave per query row; workgroups
-// stride over the units and return at once when nothing was flagged.
-constexpr int FB_WAVES = 4;
-
-__device__ __forceinline__ float fb_dot(const bf16* __restrict__ a, const bf16* __restrict__ b) {
-  float acc = 0.f;
-#pragma unroll 4
-  for (int t = 0; t < DH; t += 8) {
-    const bf16x8 x = *(const bf16x8*)(a + t);
-    const bf16x8 y = *(const bf16x8*)(b + t);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(to_f32(x[i]), to_f32(y[i]), acc);
-  }
-  return acc;
-}
-
-__global__ __launch_bounds__(FB_WAVES * 64) void block_attn_bf16_fallback_kernel(
-    const bf16* __restrict__ qkv, const int4* __restrict__ table,
-    const unsigned long long* __restrict__ ovf, int d, float scale_log2, bf16* __restrict__ O) {
-  if (table[0].y == 0) return;
-  __shared__ float pbuf[FB_WAVES][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int units = table[0].x;
-  const int ld = 3 * d;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    unsigned long long f = ovf[u];
-    const int4 e = table[1 + u];
-    const int row0 = e.x, L = e.y, q0 = e.z, qn = e.w;
-    while (f != 0) {
-      const int h = __ffsll((long long)f) - 1;
-      f &= f - 1;
-      const bf16* kbase = qkv + (size_t)row0 * ld + d + h * DH;
-      const bf16* vbase = qkv + (size_t)row0 * ld + 2 * d + h * DH;
-      for (int i = wave; i < qn; i += FB_WAVES) {
-        const bf16* q = qkv + (size_t)(row0 + q0 + i) * ld + h * DH;
-        float mx = -INFINITY;
-        for (int j = lane; j < L; j += 64) mx = fmaxf(mx, fb_dot(q, kbase + (size_t)j * ld));
-        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        const float mref = __builtin_ceilf(mx * scale_log2);
-        float o0 = 0.f, o1 = 0.f, psum = 0.f;  // this lane's dims 2*lane, 2*lane + 1
-        for (int j0 = 0; j0 < L; j0 += 64) {
-          const int j = j0 + lane;
-          float pj = 0.f;
-          if (j < L)
-            pj = to_f32(to_bf16(__builtin_amdgcn_exp2f(
-                __builtin_fmaf(fb_dot(q, kbase + (size_t)j * ld), scale_log2, -mref))));
-          psum += pj;
-          pbuf[wave][lane] = pj;
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int jn = min(64, L - j0);
-          for (int t = 0; t < jn; ++t) {
-            const float pt = pbuf[wave][t];
-            const bf16* v = vbase + (size_t)(j0 + t) * ld + 2 * lane;
-            o0 = __builtin_fmaf(pt, to_f32(v[0]), o0);
-            o1 = __builtin_fmaf(pt, to_f32(v[1]), o1);
-          }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off);
-        const float inv = 1.f / psum;
-        bf16* op = O + (size_t)(row0 + q0 + i) * d + h * DH + 2 * lane;
-        op[0] = to_bf16(o0 * inv);
-        op[1] = to_bf16(o1 * inv);
-      }
+  // ---- items whose scores outran their reference: recompute them exactly ----
+  wait_vmcnt_le(0);  // this wave's O stores are done before anyone overwrites them
+  stream_barrier();
+  const int nflag = flist[0];
+  if (nflag == 0) return;
+  if (nflag <= ATT_FLIST) {
+    for (int i = 0; i < nflag; ++i) {
+      const int v = flist[1 + i];
+      const int u = v / heads;
+      exact_item(qkv, table[1 + u], v - u * heads, d, scale_log2, O, wave, ATT_PRODUCER, pbuf[wave]);
+    }
+  } else {  // more than the list holds: check every item of this workgroup
+    Cursor c;
+    c.r = 0;
+    for (cursor_load(c, table, items, heads); c.valid; ++c.r, cursor_load(c, table, items, heads)) {
+      const int u = c.v / heads;
+      if ((__atomic_load_n(&ovf[u], __ATOMIC_RELAXED) >> c.h) & 1)
+        exact_item(qkv, table[1 + u], c.h, d, scale_log2, O, wave, ATT_PRODUCER, pbuf[wave]);
     }
   }
 }
@@ -710,12 +724,6 @@ hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long lo
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
   hipLaunchKernelGGL(block_attn_bf16_kernel, dim3(grid), dim3(ATT_THREADS), 0, stream,
                      (const bf16*)qkv, (int4*)table, ovf, heads, d, scale_log2, (bf16*)o);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int fgrid = units < 64 ? (int)units : 64;
-  hipLaunchKernelGGL(block_attn_bf16_fallback_kernel, dim3(fgrid), dim3(FB_WAVES * 64), 0, stream,
-                     (const bf16*)qkv, (const int4*)table, (const unsigned long long*)ovf, d, scale_log2,
-                     (bf16*)o);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ __device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnU
 }
 
 // Unit table for kernels that read their units with scalar loads.
-// table[0] = {number of units, 0, 0, 0} (.y counts flagged items afterwards);
+// table[0] = {number of units, 0, 0, 0};
 // table[1 + i] = {row0, L, q0, qn} of the i-th
 // unit in order of decreasing cost, the cost being the number of key chunks
 // of KC keys a unit takes, ceil(L/KC) (capped at 1023; the order of units of
