@@ -6,35 +6,38 @@
 //   O_h = softmax(Q_h K_h^T / sqrt(128)) V_h
 // reading Q|K|V from the projection output qkv[N][3d] and writing O[N][d].
 //
-// Work item = (unit, head), unit = (block, group of up to 256 query rows),
-// taken from a unit table built on the device from cu_seqlens, sorted by cost
-// (read here with scalar loads).
+// Work item = (unit, head), unit = (block, group of up to 224 query rows),
+// taken from a unit table built on the device from cu_seqlens and sorted by
+// cost (read here with scalar loads).  Persistent workgroups, one per CU, each
+// take one item per round in snake order over the sorted table.
 //
-// Persistent workgroups, one per CU (8 waves), each taking one item per round
-// in snake order over the sorted table.  All operands stream through one LDS ring of NST
-// stages of 16 KB filled by 16-byte global->LDS direct copies: an item
-// contributes its query stages (64 rows each), then its key chunks (32 K
-// rows + 32 V rows).  Copies run NST-1 stages ahead of the math, across item
-// boundaries, so the memory pipe does not drain between items.  Each wave
-// counts its own vector-memory operations, so the wait before a stage allows
-// exactly the operations issued after that stage's copies (later copies and
-// O stores) to stay in flight.
+// A workgroup is 7 math waves (32 query rows each) and one copy wave:
+//   * the copy wave streams the K|V rows of its items, 32 keys per stage,
+//     through an LDS ring of 8 stages of 16 KB with 16-byte global->LDS direct
+//     copies, 4 stages ahead and across item boundaries, and waits for each
+//     stage's copies before the stage's workgroup barrier; the math waves
+//     never issue ring copies (a copy issued behind a saturated memory pipe
+//     holds its wave for hundreds of cycles);
+//   * a math wave loads the Q fragments of its rows of the next item into a
+//     second register set with plain global loads while the current item
+//     runs.
 //
-// Math per wave (32 query rows = two 16-row tiles), v_mfma_f32_16x16x32_bf16:
+// Math per math wave and key chunk, v_mfma_f32_16x16x32_bf16:
 //   * S^T = K Q^T: the K rows of the two 16-key tiles of a chunk are permuted
 //     so that a lane's scores for both tiles are 8 consecutive keys -- the P^T
 //     operand layout of the PV product; P never leaves registers;
 //   * O^T += V^T P^T: the V^T operand is read straight from the row-major V
-//     rows with the transposing LDS read ds_read_b64_tr_b16 (per 16-lane
-//     group, lane j receives element j%4 of the 8-byte pieces addressed by
-//     lanes j/4 + 4s, s = 0..3);
-//   * online softmax in base 2 with fp32 running max and sum; the max is
-//     reduced across the 4 lane groups holding one query, the sum at the end;
-//     P is rounded to bf16 (RNE) for the MFMA and the sum uses the rounded
+//     rows with the transposing LDS read ds_read_b64_tr_b16; the row sums of
+//     P come from the same product with an all-ones operand;
+//   * softmax in base 2 against a per-row reference fixed at the item's first
+//     chunk (an integer: the ceiling of that chunk's row max, so P rounds to
+//     bf16 as it would against the true max); later scores may exceed it by
+//     up to 2^REF_HEADROOM, beyond which the item is flagged and recomputed
+//     exactly at the end of the kernel;
+//   * P is rounded to bf16 (RNE) for the MFMA and the sums use the rounded
 //     values; O = acc / sum is rounded once to bf16;
-//   * rows past the block end are copied from its last row (finite data),
-//     keys past it are masked to -inf, and key tiles or query tiles lying
-//     wholly past the end are skipped.
+//   * rows past the block end are copies of its last row (finite data) and
+//     keys past it are masked to -inf.
 #include "attn_units.hpp"
 
 namespace gs {
