@@ -38,6 +38,8 @@
 //     values; O = acc / sum is rounded once to bf16;
 //   * rows past the block end are copies of its last row (finite data) and
 //     keys past it are masked to -inf.
+#include <type_traits>
+
 #include "attn_units.hpp"
 
 namespace gs {
@@ -142,6 +144,25 @@ __device__ __forceinline__ void score_tiles2(const bf16x8 (*k)[4], const bf16x8*
       : "v"(k[0][0]), "v"(k[0][1]), "v"(k[0][2]), "v"(k[0][3]), "v"(k[1][0]), "v"(k[1][1]),
         "v"(k[1][2]), "v"(k[1][3]), "v"(q0[0]), "v"(q0[1]), "v"(q0[2]), "v"(q0[3]), "v"(q1[0]),
         "v"(q1[1]), "v"(q1[2]), "v"(q1[3]));
+}
+
+// One query tile against the two 16-key tiles of a chunk (as score_tiles2).
+__device__ __forceinline__ void score_tiles1(const bf16x8 (*k)[4], const bf16x8* q0, f32x4& s00, f32x4& s01) {
+  asm volatile(
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %10, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %10, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %11, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %7, %11, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %12, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %8, %12, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %13, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %9, %13, %1\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 3"
+      : "=&v"(s00), "=&v"(s01)
+      : "v"(k[0][0]), "v"(k[0][1]), "v"(k[0][2]), "v"(k[0][3]), "v"(k[1][0]), "v"(k[1][1]),
+        "v"(k[1][2]), "v"(k[1][3]), "v"(q0[0]), "v"(q0[1]), "v"(q0[2]), "v"(q0[3]));
 }
 
 // Max / sum of a value over the lane pairs (l, l^32) and (l, l^16), with the
@@ -441,17 +462,22 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     return;
   }
 
+  // Row slot of a math wave: its 32 rows of an item are rslot*32 ... The wave
+  // that shares its SIMD with the copy wave (wave 3) takes the last slot, which
+  // a 200-frame block leaves mostly empty (and then runs one query tile).
+  const int rslot = wave == 3 ? ATT_PRODUCER - 1 : (wave > 3 ? wave - 1 : wave);
+
   // ---- query rows: a math wave loads the fragments of its rows of the next
   // item straight from global memory while the current item runs ----
   bf16x8 qnext[ATT_QT][4];
   int qmark = 0;  // its loads are complete once at most ops - qmark are pending
   auto load_q = [&](const Cursor& c) __attribute__((always_inline)) {
-    if (wave * ATT_QW >= c.qn) return;  // no rows for this wave
+    if (rslot * ATT_QW >= c.qn) return;  // no rows for this wave
     const int qlast = c.qn - 1;
     const bf16* blk = qkv + (size_t)(c.row0 + c.q0) * ld + c.h * DH + g4 * 8;
 #pragma unroll
     for (int tt = 0; tt < ATT_QT; ++tt) {
-      int r = wave * ATT_QW + tt * 16 + l16;
+      int r = rslot * ATT_QW + tt * 16 + l16;
       r = r <= qlast ? r : qlast;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) qnext[tt][kc] = *(const bf16x8*)(blk + (size_t)r * ld + kc * 32);
@@ -461,7 +487,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   };
   load_q(comp);
 
-  // ---- per-wave query state: rows ATT_QW*wave + 16*tt + lane%16 of the item ----
+  // ---- per-wave query state: rows ATT_QW*rslot + 16*tt + lane%16 of the item ----
   bf16x8 qf[ATT_QT][4];
 #pragma unroll
   for (int tt = 0; tt < ATT_QT; ++tt)
@@ -508,7 +534,8 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   };
   // S^T = K Q^T for the chunk in slot `sl`: tile kt row r feeds key
   // perm_key(kt, r), so a lane holds keys g4*8 + kt*4 + i of its query.
-  auto scores = [&](int sl, f32x4 (*s)[2]) __attribute__((always_inline)) {
+  auto scores = [&](auto qtc, int sl, f32x4 (*s)[2]) __attribute__((always_inline)) {
+    constexpr int QT = decltype(qtc)::value;
     const unsigned sb = ring_base + (unsigned)sl * STAGE_BYTES;
     bf16x8 kf[2][4];
 #pragma unroll
@@ -516,16 +543,18 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
         kf[kt][kc] = *(const GS_LDS bf16x8*)(uintptr_t)(sb + koff[kc] + kt * (4 * DH * 2));
-#pragma unroll
-    for (int tt = 0; tt < ATT_QT; tt += 2)
-      score_tiles2(kf, qf[tt], qf[tt + 1], s[tt][0], s[tt][1], s[tt + 1][0], s[tt + 1][1]);
+    if constexpr (QT == 2)
+      score_tiles2(kf, qf[0], qf[1], s[0][0], s[0][1], s[1][0], s[1][1]);
+    else
+      score_tiles1(kf, qf[0], s[0][0], s[0][1]);
   };
   // Masks keys past the block end (a block's partial last chunk) and returns
   // this lane's max raw score per query tile.
-  auto mask_max = [&](f32x4 (*s)[2], int kvalid, float* lmax) __attribute__((always_inline)) {
+  auto mask_max = [&](auto qtc, f32x4 (*s)[2], int kvalid, float* lmax) __attribute__((always_inline)) {
+    constexpr int QT = decltype(qtc)::value;
     if (kvalid < ATT_KC) {
 #pragma unroll
-      for (int tt = 0; tt < ATT_QT; ++tt)
+      for (int tt = 0; tt < QT; ++tt)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -533,14 +562,15 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
             if (g4 * 8 + kt * 4 + i >= kvalid) s[tt][kt][i] = -INFINITY;
     }
 #pragma unroll
-    for (int tt = 0; tt < ATT_QT; ++tt)
+    for (int tt = 0; tt < QT; ++tt)
       lmax[tt] = fmaxf(fmaxf(fmaxf(s[tt][0][0], s[tt][0][1]), fmaxf(s[tt][0][2], s[tt][0][3])),
                        fmaxf(fmaxf(s[tt][1][0], s[tt][1][1]), fmaxf(s[tt][1][2], s[tt][1][3])));
   };
   // P = exp2(s*scale - mref), rounded to bf16, in the PV operand layout
-  auto probs = [&](f32x4 (*s)[2], const float* mref, bf16x8* pn) __attribute__((always_inline)) {
+  auto probs = [&](auto qtc, f32x4 (*s)[2], const float* mref, bf16x8* pn) __attribute__((always_inline)) {
+    constexpr int QT = decltype(qtc)::value;
 #pragma unroll
-    for (int tt = 0; tt < ATT_QT; ++tt)
+    for (int tt = 0; tt < QT; ++tt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -552,7 +582,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   // ---- items ----
   for (; comp.valid; ) {
     const int nk = comp.ns;
-    const int nval = min(ATT_QW, comp.qn - wave * ATT_QW);  // this wave's query rows
+    const int nval = min(ATT_QW, comp.qn - rslot * ATT_QW);  // this wave's query rows
     const int row0 = comp.row0, L = comp.L, q0 = comp.q0, h = comp.h;
     const int uidx = comp.v / heads;  // the unit's position in the table
     // ---- this wave's query fragments, and the loads of the next item's ----
@@ -570,112 +600,121 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     if (nval <= 0) {  // no rows for this wave: only keep the stream going
       for (int kc = 0; kc < nk; ++kc, ++p) stage_begin();
     } else {
-      f32x4 oacc[ATT_QT][8];
-      f32x4 lsum[ATT_QT];  // P row sums: lsum[tt] += 1 * P^T (4 copies per lane)
-      // Reference max per query: an integer in log2 units, fixed at the item's
-      // first chunk to ceil(that chunk's row max).  Later scores may exceed it
-      // by up to 2^REF_HEADROOM (P, O and the sums stay finite in bf16/fp32);
-      // a score beyond that flags the item for the exact fallback.  With an
-      // integer reference the bf16 rounding of P is the same as with the true
-      // row max.  thr is the raw score of that limit.
-      float mref[ATT_QT], thr[ATT_QT];
-      bf16x8 pprev[ATT_QT];  // P of the previous chunk, whose PV product is pending
-      int pslot;
-      bool flagged = false;  // (wave-uniform)
-      // ---- first key chunk: sets the reference, no PV product yet ----
-      {
-        stage_begin();
-        const int sl = p & (ATT_NST - 1);
-        f32x4 s[ATT_QT][2];
-        scores(sl, s);
-        float lmax[ATT_QT];
-        mask_max(s, min(ATT_KC, L), lmax);
+      // one or two query tiles (a wave with at most 16 rows skips the second)
+      auto run_item = [&](auto qtc) __attribute__((always_inline)) {
+        constexpr int QT = decltype(qtc)::value;
+        f32x4 oacc[QT][8];
+        f32x4 lsum[QT];  // P row sums: lsum[tt] += 1 * P^T (4 copies per lane)
+        // Reference max per query: an integer in log2 units, fixed at the item's
+        // first chunk to ceil(that chunk's row max).  Later scores may exceed it
+        // by up to 2^REF_HEADROOM (P, O and the sums stay finite in bf16/fp32);
+        // a score beyond that flags the item for the exact fallback.  With an
+        // integer reference the bf16 rounding of P is the same as with the true
+        // row max.  thr is the raw score of that limit.
+        float mref[QT], thr[QT];
+        bf16x8 pprev[QT];  // P of the previous chunk, whose PV product is pending
+        int pslot;
+        bool flagged = false;  // (wave-uniform)
+        // ---- first key chunk: sets the reference, no PV product yet ----
+        {
+          stage_begin();
+          const int sl = p & (ATT_NST - 1);
+          f32x4 s[QT][2];
+          scores(qtc, sl, s);
+          float lmax[QT];
+          mask_max(qtc, s, min(ATT_KC, L), lmax);
 #pragma unroll
-        for (int tt = 0; tt < ATT_QT; ++tt) {
-          // the chunk's row max over the 4 lane groups of a query
-          mref[tt] = __builtin_ceilf(xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2);
-          thr[tt] = (mref[tt] + REF_HEADROOM) * inv_scale_log2;
-          lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int tt = 0; tt < QT; ++tt) {
+            // the chunk's row max over the 4 lane groups of a query
+            mref[tt] = __builtin_ceilf(xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2);
+            thr[tt] = (mref[tt] + REF_HEADROOM) * inv_scale_log2;
+            lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        probs(s, mref, pprev);
-        pslot = sl;
-        ++p;
-      }
-      // ---- further key chunks ----
-      for (int kc = 1; kc < nk; ++kc, ++p) {
-        stage_begin();
-        const int sl = p & (ATT_NST - 1);
-        f32x4 s[ATT_QT][2];
-        scores(sl, s);
-        __builtin_amdgcn_sched_barrier(0);
-        // V^T of the previous chunk, read while the S products run
-        bf16x8 vf[8];
-        read_vt(pslot, vf);
-        __builtin_amdgcn_sched_barrier(0);
-        float lmax[ATT_QT];
-        mask_max(s, min(ATT_KC, L - kc * ATT_KC), lmax);
-        bool over = false;
-#pragma unroll
-        for (int tt = 0; tt < ATT_QT; ++tt) over |= lmax[tt] > thr[tt];
-        if (__builtin_amdgcn_ballot_w64(over) != 0 && !flagged) {
-          flagged = true;
-          if (lane == 0) {
-            atomicOr(&ovf[uidx], 1ull << h);
-            const int pos = atomicAdd(&flist[0], 1);
-            if (pos < ATT_FLIST) flist[1 + pos] = comp.v;
+            for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          ops += 1;
+          probs(qtc, s, mref, pprev);
+          pslot = sl;
+          ++p;
         }
-        // P of this chunk and the previous chunk's PV product
-        bf16x8 pn[ATT_QT];
-        probs(s, mref, pn);
+        // ---- further key chunks ----
+        for (int kc = 1; kc < nk; ++kc, ++p) {
+          stage_begin();
+          const int sl = p & (ATT_NST - 1);
+          f32x4 s[QT][2];
+          scores(qtc, sl, s);
+          __builtin_amdgcn_sched_barrier(0);
+          // V^T of the previous chunk, read while the S products run
+          bf16x8 vf[8];
+          read_vt(pslot, vf);
+          __builtin_amdgcn_sched_barrier(0);
+          float lmax[QT];
+          mask_max(qtc, s, min(ATT_KC, L - kc * ATT_KC), lmax);
+          bool over = false;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int tt = 0; tt < ATT_QT; ++tt)
-            oacc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev[tt], oacc[tt][dt], 0, 0, 0);
-#pragma unroll
-        for (int tt = 0; tt < ATT_QT; ++tt)
-          lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[tt], lsum[tt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int tt = 0; tt < ATT_QT; ++tt) pprev[tt] = pn[tt];
-        pslot = sl;
-      }
-      // ---- the last chunk's PV product and the item's output ----
-      {
-        bf16x8 vf[8];
-        read_vt(pslot, vf);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int tt = 0; tt < ATT_QT; ++tt)
-            oacc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev[tt], oacc[tt][dt], 0, 0, 0);
-#pragma unroll
-        for (int tt = 0; tt < ATT_QT; ++tt)
-          lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[tt], lsum[tt], 0, 0, 0);
-        const int orow = row0 + q0 + wave * ATT_QW;
-#pragma unroll
-        for (int tt = 0; tt < ATT_QT; ++tt) {
-          if (tt * 16 >= nval) continue;  // wave-uniform
-          const float inv = 1.f / lsum[tt][0];
-          if (tt * 16 + l16 < nval) {
-            bf16* op = O + (size_t)(orow + tt * 16 + l16) * d + h * DH + g4 * 4;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-              bf16x4 o;
-              o[0] = to_bf16(oacc[tt][dt][0] * inv);
-              o[1] = to_bf16(oacc[tt][dt][1] * inv);
-              o[2] = to_bf16(oacc[tt][dt][2] * inv);
-              o[3] = to_bf16(oacc[tt][dt][3] * inv);
-              *(bf16x4*)(op + dt * 16) = o;
+          for (int tt = 0; tt < QT; ++tt) over |= lmax[tt] > thr[tt];
+          if (__builtin_amdgcn_ballot_w64(over) != 0 && !flagged) {
+            flagged = true;
+            if (lane == 0) {
+              atomicOr(&ovf[uidx], 1ull << h);
+              const int pos = atomicAdd(&flist[0], 1);
+              if (pos < ATT_FLIST) flist[1 + pos] = comp.v;
             }
+            ops += 1;
           }
-          ops += 8;  // issued: lane l16 = 0 of a tile with rows is in range
+          // P of this chunk and the previous chunk's PV product
+          bf16x8 pn[QT];
+          probs(qtc, s, mref, pn);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int tt = 0; tt < QT; ++tt)
+              oacc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev[tt], oacc[tt][dt], 0, 0, 0);
+#pragma unroll
+          for (int tt = 0; tt < QT; ++tt)
+            lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[tt], lsum[tt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int tt = 0; tt < QT; ++tt) pprev[tt] = pn[tt];
+          pslot = sl;
         }
-      }
+        // ---- the last chunk's PV product and the item's output ----
+        {
+          bf16x8 vf[8];
+          read_vt(pslot, vf);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int tt = 0; tt < QT; ++tt)
+              oacc[tt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev[tt], oacc[tt][dt], 0, 0, 0);
+#pragma unroll
+          for (int tt = 0; tt < QT; ++tt)
+            lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[tt], lsum[tt], 0, 0, 0);
+          const int orow = row0 + q0 + rslot * ATT_QW;
+#pragma unroll
+          for (int tt = 0; tt < QT; ++tt) {
+            if (tt * 16 >= nval) continue;  // wave-uniform
+            const float inv = 1.f / lsum[tt][0];
+            if (tt * 16 + l16 < nval) {
+              bf16* op = O + (size_t)(orow + tt * 16 + l16) * d + h * DH + g4 * 4;
+#pragma unroll
+              for (int dt = 0; dt < 8; ++dt) {
+                bf16x4 o;
+                o[0] = to_bf16(oacc[tt][dt][0] * inv);
+                o[1] = to_bf16(oacc[tt][dt][1] * inv);
+                o[2] = to_bf16(oacc[tt][dt][2] * inv);
+                o[3] = to_bf16(oacc[tt][dt][3] * inv);
+                *(bf16x4*)(op + dt * 16) = o;
+              }
+            }
+            ops += 8;  // issued: lane l16 = 0 of a tile with rows is in range
+          }
+        }
+    
+      };
+      if (nval > 16)
+        run_item(std::integral_constant<int, 2>{});
+      else
+        run_item(std::integral_constant<int, 1>{});
     }
     comp = nxt;  // (the compute cursor only moves item by item)
   }
