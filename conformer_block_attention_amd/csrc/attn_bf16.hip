@@ -8,7 +8,8 @@
 //
 // Work item = (unit, head), unit = (block, group of up to 224 query rows),
 // taken from a unit table built on the device from cu_seqlens and sorted by
-// cost (read here with scalar loads).  Persistent workgroups, one per CU, each
+// cost (a math wave reads the entry of the item after next with a vector load one
+// item ahead).  Persistent workgroups, one per CU, each
 // take one item per round in snake order over the sorted table.
 //
 // A workgroup is 7 math waves (32 query rows each) and one copy wave:
@@ -256,18 +257,23 @@ struct Cursor {
   int ns;      // key chunks of the item
 };
 
-__device__ __forceinline__ void cursor_load(Cursor& c, const int4* __restrict__ table, int items,
-                                            int heads) {
+__device__ __forceinline__ void cursor_index(Cursor& c, int items) {
   c.v = c.r * (int)gridDim.x + ((c.r & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x);
   c.valid = c.v < items;
   c.s = 0;
-  if (c.valid) {
-    const int u = c.v / heads;
-    const int4 e = table[1 + u];  // wave-uniform address: scalar load
-    c.h = c.v - u * heads;
-    c.row0 = e.x; c.L = e.y; c.q0 = e.z; c.qn = e.w;
-    c.ns = (c.L + ATT_KC - 1) / ATT_KC;
-  }
+}
+
+// The item's fields from its unit's table entry e.
+__device__ __forceinline__ void cursor_fill(Cursor& c, int4 e, int heads) {
+  c.h = c.v - (c.v / heads) * heads;
+  c.row0 = e.x; c.L = e.y; c.q0 = e.z; c.qn = e.w;
+  c.ns = (c.L + ATT_KC - 1) / ATT_KC;
+}
+
+__device__ __forceinline__ void cursor_load(Cursor& c, const int4* __restrict__ table, int items,
+                                            int heads) {
+  cursor_index(c, items);
+  if (c.valid) cursor_fill(c, table[1 + c.v / heads], heads);  // uniform address: scalar load
 }
 
 __device__ __forceinline__ void cursor_next(Cursor& c, const int4* __restrict__ table, int items,
@@ -276,6 +282,20 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int4* __restrict__ 
     ++c.r;
     cursor_load(c, table, items, heads);
   }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(unsigned, bf16x2{to_bf16(a), to_bf16(b)});
+}
+
+// v_permlane16_swap: x's odd 16-lane groups trade places with y's even ones.
+__device__ __forceinline__ void swap_row_pairs(unsigned& x, unsigned& y) {
+  const auto s = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  x = s[0];
+  y = s[1];
 }
 
 // Exact attention for one item (unit u of the table, head h) whose scores ran
@@ -468,11 +488,14 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   const int rslot = wave == 3 ? ATT_PRODUCER - 1 : (wave > 3 ? wave - 1 : wave);
 
   // ---- query rows: a math wave loads the fragments of its rows of the next
-  // item straight from global memory while the current item runs ----
+  // item straight from global memory while the current item runs, and moves
+  // them to its working set at the end of the current item's last product,
+  // before that item's output stores (the wait for the loads then never
+  // waits for stores).  The loads are unconditional -- rows past the unit
+  // read its last row -- so that no copy of an older value, with a wait for
+  // every load in flight, lands on the item boundary. ----
   bf16x8 qnext[ATT_QT][4];
-  int qmark = 0;  // its loads are complete once at most ops - qmark are pending
   auto load_q = [&](const Cursor& c) __attribute__((always_inline)) {
-    if (rslot * ATT_QW >= c.qn) return;  // no rows for this wave
     const int qlast = c.qn - 1;
     const bf16* blk = qkv + (size_t)(c.row0 + c.q0) * ld + c.h * DH + g4 * 8;
 #pragma unroll
@@ -482,17 +505,41 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) qnext[tt][kc] = *(const bf16x8*)(blk + (size_t)r * ld + kc * 32);
     }
-    ops += 4 * ATT_QT;
-    qmark = ops;
+  };
+  // ---- per-wave query state: rows ATT_QW*rslot + 16*tt + lane%16 of the item ----
+  // Working set <- the loaded fragments.  The empty asm makes the working set
+  // a value of its own, defined at this point: a plain copy would turn into a
+  // register copy at the end of the loop, after the stores, with its wait,
+  // and the loads' registers would carry their pending state into the loop.
+  bf16x8 qf[ATT_QT][4];
+  auto take_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int tt = 0; tt < ATT_QT; ++tt)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) asm volatile("" : "=v"(qf[tt][kc]) : "0"(qnext[tt][kc]));
   };
   load_q(comp);
+  take_q();
 
-  // ---- per-wave query state: rows ATT_QW*rslot + 16*tt + lane%16 of the item ----
-  bf16x8 qf[ATT_QT][4];
-#pragma unroll
-  for (int tt = 0; tt < ATT_QT; ++tt)
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) qf[tt][kc] = bf16x8{};  // tiles without rows stay finite
+  // ---- items ahead: the next item's cursor, and the table entry of the one
+  // after it, loaded with a vector load at the start of an item (an address
+  // the compiler sees as per-lane) and read out at the point above, so that
+  // no scalar-load latency falls on the item boundary ----
+  Cursor nxt;
+  nxt.r = comp.r + 1;
+  cursor_load(nxt, table, items, heads);
+  int vzero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+  int4 epre;
+  int e2x = 0, e2y = 0, e2z = 0, e2w = 0;  // the entry after the next item's (uniform)
+  // working set <- next item's Q; entry after next -> SGPRs
+  auto take_next = [&]() __attribute__((always_inline)) {
+    take_q();
+    e2x = __builtin_amdgcn_readfirstlane(epre.x);
+    e2y = __builtin_amdgcn_readfirstlane(epre.y);
+    e2z = __builtin_amdgcn_readfirstlane(epre.z);
+    e2w = __builtin_amdgcn_readfirstlane(epre.w);
+  };
   const float inv_scale_log2 = 1.f / scale_log2;
   bf16x8 ones;
 #pragma unroll
@@ -585,20 +632,17 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     const int nval = min(ATT_QW, comp.qn - rslot * ATT_QW);  // this wave's query rows
     const int row0 = comp.row0, L = comp.L, q0 = comp.q0, h = comp.h;
     const int uidx = comp.v / heads;  // the unit's position in the table
-    // ---- this wave's query fragments, and the loads of the next item's ----
-    Cursor nxt;
-    nxt.r = comp.r + 1;
-    cursor_load(nxt, table, items, heads);
-    if (nval > 0) {
-      wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - qmark));
-#pragma unroll
-      for (int tt = 0; tt < ATT_QT; ++tt)
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) qf[tt][kc] = qnext[tt][kc];
+    // ---- loads for the items ahead: the entry after next, the next item's Q ----
+    {
+      Cursor t;
+      t.r = nxt.r + 1;
+      cursor_index(t, items);
+      epre = table[1 + (t.valid ? t.v / heads : 0) + vzero];  // (unconditional, as for Q)
     }
-    if (nxt.valid) load_q(nxt);
+    load_q(nxt.valid ? nxt : comp);
     if (nval <= 0) {  // no rows for this wave: only keep the stream going
       for (int kc = 0; kc < nk; ++kc, ++p) stage_begin();
+      take_next();
     } else {
       // one or two query tiles (a wave with at most 16 rows skips the second)
       auto run_item = [&](auto qtc) __attribute__((always_inline)) {
@@ -659,7 +703,6 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
               const int pos = atomicAdd(&flist[0], 1);
               if (pos < ATT_FLIST) flist[1 + pos] = comp.v;
             }
-            ops += 1;
           }
           // P of this chunk and the previous chunk's PV product
           bf16x8 pn[QT];
@@ -689,24 +732,29 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
 #pragma unroll
           for (int tt = 0; tt < QT; ++tt)
             lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[tt], lsum[tt], 0, 0, 0);
+          take_next();
+          // O rows, 16 bytes per lane: lane (g4, l16) holds dh dt*16 + 4*g4 ..
+          // +3 of its row.  For a pair of tiles dt, dt+1, v_permlane16_swap
+          // trades the odd lane groups' dt values for the even groups' dt+1
+          // values, so an even group g4 ends with dh dt*16 + 4*g4 .. +7 and an
+          // odd group with dh (dt+1)*16 + 4*(g4-1) .. +7.
           const int orow = row0 + q0 + rslot * ATT_QW;
 #pragma unroll
           for (int tt = 0; tt < QT; ++tt) {
             if (tt * 16 >= nval) continue;  // wave-uniform
             const float inv = 1.f / lsum[tt][0];
-            if (tt * 16 + l16 < nval) {
-              bf16* op = O + (size_t)(orow + tt * 16 + l16) * d + h * DH + g4 * 4;
+            bf16* op = O + (size_t)(orow + tt * 16 + l16) * d + h * DH + (g4 & 1) * 16 + (g4 >> 1) * 8;
+            const bool row_ok = tt * 16 + l16 < nval;
 #pragma unroll
-              for (int dt = 0; dt < 8; ++dt) {
-                bf16x4 o;
-                o[0] = to_bf16(oacc[tt][dt][0] * inv);
-                o[1] = to_bf16(oacc[tt][dt][1] * inv);
-                o[2] = to_bf16(oacc[tt][dt][2] * inv);
-                o[3] = to_bf16(oacc[tt][dt][3] * inv);
-                *(bf16x4*)(op + dt * 16) = o;
-              }
+            for (int dt = 0; dt < 8; dt += 2) {
+              unsigned x0 = pack_bf16x2(oacc[tt][dt][0] * inv, oacc[tt][dt][1] * inv);
+              unsigned x1 = pack_bf16x2(oacc[tt][dt][2] * inv, oacc[tt][dt][3] * inv);
+              unsigned y0 = pack_bf16x2(oacc[tt][dt + 1][0] * inv, oacc[tt][dt + 1][1] * inv);
+              unsigned y1 = pack_bf16x2(oacc[tt][dt + 1][2] * inv, oacc[tt][dt + 1][3] * inv);
+              swap_row_pairs(x0, y0);
+              swap_row_pairs(x1, y1);
+              if (row_ok) *(u32x4*)(op + dt * 16) = u32x4{x0, x1, y0, y1};
             }
-            ops += 8;  // issued: lane l16 = 0 of a tile with rows is in range
           }
         }
     
@@ -717,6 +765,9 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         run_item(std::integral_constant<int, 1>{});
     }
     comp = nxt;  // (the compute cursor only moves item by item)
+    nxt.r = comp.r + 1;
+    cursor_index(nxt, items);
+    if (nxt.valid) cursor_fill(nxt, int4{e2x, e2y, e2z, e2w}, heads);
   }
   // ---- items whose scores outran their reference: recompute them exactly ----
   wait_vmcnt_le(0);  // this wave's O stores are done before anyone overwrites them
