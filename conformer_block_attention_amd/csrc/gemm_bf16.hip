@@ -491,9 +491,14 @@ static int gemm_persistent_grid(int tiles) {
   return tiles < g_gemm_cus ? tiles : g_gemm_cus;
 }
 
+hipError_t launch_qkv_proj_bf16_pp(const void* x, const void* wqkv, void* qkv, int M, int d,
+                                   hipStream_t stream);
+
 hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int M, int d,
                                 hipStream_t stream) {
-  // 3d = 384 * heads is always a multiple of 192
+  // 3d is a multiple of 256 when d is (two waves per SIMD, 256 x 256 tiles);
+  // otherwise 3d = 384 * (d / 128) is a multiple of 192
+  if ((3 * d) % 256 == 0) return launch_qkv_proj_bf16_pp(x, wqkv, qkv, M, d, stream);
   const int Nc = 3 * d;
   const int mt = (M + GEMM_BM - 1) / GEMM_BM;
   hipLaunchKernelGGL((gemm_bf16_nt_kernel<192, 64, 2, false, 0, 12, false>), dim3(gemm_persistent_grid(mt * (Nc / 192))),
@@ -502,8 +507,12 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int 
   return hipGetLastError();
 }
 
+hipError_t launch_out_proj_bf16_pp(const void* o, const void* wo, const void* x, void* out, int M,
+                                   int d, hipStream_t stream);
+
 hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
                                 int d, hipStream_t stream) {
+  if (d % 256 == 0) return launch_out_proj_bf16_pp(o, wo, x, out, M, d, stream);
   const int mt = (M + GEMM_BM - 1) / GEMM_BM;
   hipLaunchKernelGGL((gemm_bf16_nt_kernel<128, 64, 3, false, 0, 8, true>), dim3(gemm_persistent_grid(mt * (d / 128))),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)o, (const bf16*)wo,
