@@ -30,8 +30,8 @@ F32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 KERNELS = ("qkv_proj", "block_attn", "out_proj")
 KERNEL_SOURCES = {
-    "qkv_proj": ["gemm_bf16.hip"],
-    "out_proj": ["gemm_bf16.hip"],
+    "qkv_proj": ["gemm_bf16.hip", "gemm_pp_bf16.hip"],
+    "out_proj": ["gemm_bf16.hip", "gemm_pp_bf16.hip"],
     "block_attn": ["attn_bf16.hip", "attn_units.hpp"],
 }
 
