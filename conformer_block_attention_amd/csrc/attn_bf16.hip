@@ -31,10 +31,12 @@
 //     rows with the transposing LDS read ds_read_b64_tr_b16; the row sums of
 //     P come from the same product with an all-ones operand;
 //   * softmax in base 2 against a per-row reference fixed at the item's first
-//     chunk (an integer: the ceiling of that chunk's row max, so P rounds to
-//     bf16 as it would against the true max); later scores may exceed it by
-//     up to 2^REF_HEADROOM, beyond which the item is flagged and recomputed
-//     exactly at the end of the kernel;
+//     chunk (an integer: the ceiling of that chunk's row max); later scores
+//     may exceed it by any amount: P then carries an exact power-of-two
+//     factor, rounds to bf16 as it would against the true max, and cancels in
+//     O = acc / sum.  Only a P, sum or accumulator that overflows can break
+//     that; an item whose row sums or accumulators end non-finite is flagged
+//     and recomputed exactly at the end of the kernel;
 //   * P is rounded to bf16 (RNE) for the MFMA and the sums use the rounded
 //     values; O = acc / sum is rounded once to bf16;
 //   * rows past the block end are copies of its last row (finite data) and
@@ -189,7 +191,6 @@ __device__ __forceinline__ float xsum_lanes16(float x) {
 // Scores may exceed an item's reference max by this many doublings before the
 // item is handed to the exact fallback: P <= 2^64, and O and the row sums of
 // at most 2^31 keys stay far inside fp32 range for any |V| < 2^32.
-constexpr float REF_HEADROOM = 64.f;
 
 // Workgroup barrier without a memory fence.  A fence would make every wave
 // wait for all of its outstanding global->LDS copies and global stores; the
@@ -298,9 +299,10 @@ __device__ __forceinline__ void swap_row_pairs(unsigned& x, unsigned& y) {
   y = s[1];
 }
 
-// Exact attention for one item (unit u of the table, head h) whose scores ran
-// more than REF_HEADROOM doublings above its reference (never seen with
-// logits of ordinary size).  Two passes over the keys per query row: the row
+// Exact attention for one item (unit u of the table, head h) whose row sums
+// or accumulators overflowed against the first chunk's reference (its scores
+// ran about 100 doublings or more above it; never seen with logits of
+// ordinary size).  Two passes over the keys per query row: the row
 // max, then P with the rounding of the fast path (reference = ceil of the row
 // max in log2 units, P rounded to bf16, the sum taken over the rounded values)
 // and O = sum_j P_j V_j / sum_j P_j, rounded once to bf16.  Waves w0, w0 +
@@ -540,7 +542,6 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     e2z = __builtin_amdgcn_readfirstlane(epre.z);
     e2w = __builtin_amdgcn_readfirstlane(epre.w);
   };
-  const float inv_scale_log2 = 1.f / scale_log2;
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
@@ -595,9 +596,8 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
     else
       score_tiles1(kf, qf[0], s[0][0], s[0][1]);
   };
-  // Masks keys past the block end (a block's partial last chunk) and returns
-  // this lane's max raw score per query tile.
-  auto mask_max = [&](auto qtc, f32x4 (*s)[2], int kvalid, float* lmax) __attribute__((always_inline)) {
+  // Masks keys past the block end (a block's partial last chunk).
+  auto mask = [&](auto qtc, f32x4 (*s)[2], int kvalid) __attribute__((always_inline)) {
     constexpr int QT = decltype(qtc)::value;
     if (kvalid < ATT_KC) {
 #pragma unroll
@@ -608,6 +608,11 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           for (int i = 0; i < 4; ++i)
             if (g4 * 8 + kt * 4 + i >= kvalid) s[tt][kt][i] = -INFINITY;
     }
+  };
+  // ... and returns this lane's max raw score per query tile.
+  auto mask_max = [&](auto qtc, f32x4 (*s)[2], int kvalid, float* lmax) __attribute__((always_inline)) {
+    constexpr int QT = decltype(qtc)::value;
+    mask(qtc, s, kvalid);
 #pragma unroll
     for (int tt = 0; tt < QT; ++tt)
       lmax[tt] = fmaxf(fmaxf(fmaxf(s[tt][0][0], s[tt][0][1]), fmaxf(s[tt][0][2], s[tt][0][3])),
@@ -650,15 +655,14 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         f32x4 oacc[QT][8];
         f32x4 lsum[QT];  // P row sums: lsum[tt] += 1 * P^T (4 copies per lane)
         // Reference max per query: an integer in log2 units, fixed at the item's
-        // first chunk to ceil(that chunk's row max).  Later scores may exceed it
-        // by up to 2^REF_HEADROOM (P, O and the sums stay finite in bf16/fp32);
-        // a score beyond that flags the item for the exact fallback.  With an
-        // integer reference the bf16 rounding of P is the same as with the true
-        // row max.  thr is the raw score of that limit.
-        float mref[QT], thr[QT];
+        // first chunk to ceil(that chunk's row max).  Later scores may exceed it:
+        // with an integer reference P differs from P against the true row max
+        // by an exact power of two, so it rounds to bf16 the same way and the
+        // factor cancels in acc / sum, unless something overflows (checked at
+        // the end of the item).
+        float mref[QT];
         bf16x8 pprev[QT];  // P of the previous chunk, whose PV product is pending
         int pslot;
-        bool flagged = false;  // (wave-uniform)
         // ---- first key chunk: sets the reference, no PV product yet ----
         {
           stage_begin();
@@ -671,7 +675,6 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           for (int tt = 0; tt < QT; ++tt) {
             // the chunk's row max over the 4 lane groups of a query
             mref[tt] = __builtin_ceilf(xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2);
-            thr[tt] = (mref[tt] + REF_HEADROOM) * inv_scale_log2;
             lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -691,19 +694,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           bf16x8 vf[8];
           read_vt(pslot, vf);
           __builtin_amdgcn_sched_barrier(0);
-          float lmax[QT];
-          mask_max(qtc, s, min(ATT_KC, L - kc * ATT_KC), lmax);
-          bool over = false;
-#pragma unroll
-          for (int tt = 0; tt < QT; ++tt) over |= lmax[tt] > thr[tt];
-          if (__builtin_amdgcn_ballot_w64(over) != 0 && !flagged) {
-            flagged = true;
-            if (lane == 0) {
-              atomicOr(&ovf[uidx], 1ull << h);
-              const int pos = atomicAdd(&flist[0], 1);
-              if (pos < ATT_FLIST) flist[1 + pos] = comp.v;
-            }
-          }
+          mask(qtc, s, min(ATT_KC, L - kc * ATT_KC));
           // P of this chunk and the previous chunk's PV product
           bf16x8 pn[QT];
           probs(qtc, s, mref, pn);
@@ -733,6 +724,25 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           for (int tt = 0; tt < QT; ++tt)
             lsum[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[tt], lsum[tt], 0, 0, 0);
           take_next();
+          // Overflow: a non-finite row sum or accumulator (inf or NaN: all
+          // exponent bits set) flags the item for the exact recomputation.
+          {
+            unsigned big = 0;
+#pragma unroll
+            for (int tt = 0; tt < QT; ++tt) {
+              big = max(big, __builtin_bit_cast(unsigned, lsum[tt][0]) & 0x7fffffffu);
+#pragma unroll
+              for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  big = max(big, __builtin_bit_cast(unsigned, oacc[tt][dt][i]) & 0x7fffffffu);
+            }
+            if (__builtin_amdgcn_ballot_w64(big >= 0x7f800000u) != 0 && lane == 0) {
+              atomicOr(&ovf[uidx], 1ull << h);
+              const int pos = atomicAdd(&flist[0], 1);
+              if (pos < ATT_FLIST) flist[1 + pos] = comp.v;
+            }
+          }
           // O rows, 16 bytes per lane: lane (g4, l16) holds dh dt*16 + 4*g4 ..
           // +3 of its row.  For a pair of tiles dt, dt+1, v_permlane16_swap
           // trades the odd lane groups' dt values for the even groups' dt+1

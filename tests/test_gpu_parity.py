@@ -112,16 +112,20 @@ def test_stage_block_attn(orc, dtype, lengths, B):
 
 def test_stage_block_attn_large_logits(orc):
     """Logits far above those of an item's first key chunk.  The bf16 kernel fixes
-    a per-row reference at the first chunk and hands an item to its exact
-    two-pass fallback once a later score exceeds it by more than 64 doublings
-    (raw score > 64 / log2(e) * sqrt(128) = 502 here); below that the large
-    weights stay inside the fast path.
-      block 0, head 0: keys 0..31 zero, key 100 and all queries = 7 (score 554):
-                        every row goes to the fallback
+    a per-row reference at the first chunk; later scores above it give P an
+    exact power-of-two factor that cancels in O, and the item goes to the
+    exact two-pass fallback only when a row sum or accumulator overflows
+    (about 2^128: a score some 128 doublings or more above the reference,
+    raw score > 128 / log2(e) * sqrt(128) = 1004 here with N(0, 1) values).
+      block 0, head 0: keys 0..31 zero, key 100 and all queries = 7 (score 554,
+                        800 doublings): every row goes to the fallback
       block 0, head 1: keys 0..31 zero, key 195 (partial last chunk) = 7 and
                         queries = 7: fallback, decided in the masked chunk
       block 1, head 1: keys 0..31 zero, key 50 and queries = 6 (score 407):
                         fast path with weights up to 2^52
+      block 2, head 0: keys 0..31 zero, key 50 and queries = 2.47 (about
+                        2^100 above the first chunk's reference, nothing
+                        overflows): fast path
     Everything else is N(0, 1)."""
     G.print_case("stage_block_attn_large_logits")
     d, H, B = 256, 2, 200
@@ -140,6 +144,9 @@ def test_stage_block_attn_large_logits(orc):
     qkv[k(slice(200, 232), 1)] = 0.0
     qkv[k(250, 1)] = 6.0
     qkv[q(slice(200, 330), 1)] = 6.0
+    qkv[k(slice(330, 362), 0)] = 0.0
+    qkv[k(380, 0)] = 2.47
+    qkv[q(slice(330, 420), 0)] = 2.47
     qkv_cpu = qkv.to(torch.bfloat16)
     cu = workloads.cu_seqlens(lengths)
     o = gsattn.block_attn(qkv_cpu.to(G.dev()), torch.from_numpy(cu).to(G.dev()), H, B)
