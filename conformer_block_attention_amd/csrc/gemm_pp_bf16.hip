@@ -420,12 +420,36 @@ hipError_t launch_qkv_proj_bf16_pp(const void* x, const void* wqkv, void* qkv, i
   return hipGetLastError();
 }
 
+// Load balance: when the 256 x 256 tiles leave a partial last round that
+// 256 x 128 tiles can finish in one round, the rows of the whole rounds run
+// first and the remaining panels follow as a second launch of half-width
+// tiles (for d = 1024 on 256 CUs: 192 panels in 3 rounds, then 24 panels as
+// 192 tiles, instead of 4 rounds for 3.4 rounds of work).
 hipError_t launch_out_proj_bf16_pp(const void* o, const void* wo, const void* x, void* out, int M,
                                    int d, hipStream_t stream) {
   const int mt = (M + pp::BM - 1) / pp::BM;
-  hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, true, 2>), dim3(pp_persistent_grid(mt * (d / 256))),
+  const int nt = d / 256;
+  const int cus = pp_persistent_grid(1 << 30);
+  int main_panels = mt;
+  if (mt * nt > cus && cus % nt == 0) {
+    const int per_round = cus / nt;  // panels per round of 256 x 256 tiles
+    const int rounds = mt / per_round;
+    const int rest = mt - rounds * per_round;
+    if (rounds >= 1 && rest > 0 && rest * 2 * nt <= cus) main_panels = rounds * per_round;
+  }
+  const int m1 = min(M, main_panels * pp::BM);
+  hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, true, 2>), dim3(pp_persistent_grid(main_panels * nt)),
                      dim3(pp::THREADS), 0, stream, (const bf16*)o, (const bf16*)wo, (const bf16*)x,
-                     (bf16*)out, M, d, d);
+                     (bf16*)out, m1, d, d);
+  if (m1 < M) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t off = (size_t)m1 * d;
+    hipLaunchKernelGGL((gemm_pp_bf16_kernel<128, true, 2>),
+                       dim3(pp_persistent_grid((mt - main_panels) * 2 * nt)), dim3(pp::THREADS), 0, stream,
+                       (const bf16*)o + off, (const bf16*)wo, (const bf16*)x + off, (bf16*)out + off, M - m1,
+                       d, d);
+  }
   return hipGetLastError();
 }
 

@@ -178,6 +178,28 @@ def test_stage_out_proj(orc, dtype):
     assert worst <= 1.0, worst
 
 
+def test_stage_out_proj_tail_launch(orc):
+    """17000 rows, d = 1024: 67 panels of 256 rows, more 256 x 256 tiles than CUs.
+    The bf16 path runs the first 64 panels in whole rounds and the last 3 as a
+    second launch of 256 x 128 tiles; both parts are checked."""
+    G.print_case("stage_out_proj_tail_launch")
+    n = 17000
+    case = workloads.custom_case([n], 1024, 8, 200, torch.bfloat16, seed=4)
+    g = torch.Generator().manual_seed(5)
+    o_cpu = torch.randn(n, 1024, generator=g).to(torch.bfloat16)
+    x, _, _, wo = G.on_dev(case)
+    out = gsattn.out_proj_residual(o_cpu.to(G.dev()), wo, x)
+    torch.cuda.synchronize()
+    ref = orc.out_proj_residual(o_cpu, case.weights[0][1], case.x)
+    got = out.double().cpu().numpy()
+    bound = _gemm_bound(o_cpu.double().numpy(), case.weights[0][1].double().numpy(), ref, torch.bfloat16)
+    bound += 1.01 * U_F32 * np.abs(ref)  # the residual add in fp32
+    worst = float(np.max(np.abs(got - ref) / bound))
+    tail = float(np.max(np.abs(got[64 * 256:] - ref[64 * 256:]) / bound[64 * 256:]))
+    print(f"  worst error / bound = {worst:.3f} (rows past 16384: {tail:.3f})", flush=True)
+    assert worst <= 1.0, worst
+
+
 # ---------------------------------------------------------------------------
 # the five workloads
 
