@@ -28,10 +28,12 @@
 //     l+32's 4-column halves of the transposed accumulator tile into 16-byte
 //     row pieces, stored right away.  out_proj loads the residual in the same
 //     piece layout and adds it in fp32 before the one RNE rounding.
-//   * tile order: the 8 XCDs receive workgroup ids round-robin; each XCD owns
-//     a contiguous range of 256-row panels and walks them in groups of 8
-//     panels, panel fastest, so the tiles one XCD runs at a time share a few
-//     activation panels and weight slices in its L2.
+//   * tile order: all tiles are ordered in groups of 8 panels (256-row
+//     strips), panel fastest within a group.  The 8 XCDs receive workgroup
+//     ids round-robin; each XCD owns one eighth of that order (a contiguous
+//     range, so its share differs from the others' by at most one tile) and
+//     its workgroups take its tiles in turn, so the tiles one XCD runs at a
+//     time share a few activation panels and weight slices in its L2.
 //   * rows >= M are read as row M-1, so their results equal row M-1's bit for
 //     bit; stores need no mask (a duplicate row writes the same bits).
 //     Requires K % 64 == 0 and Nc % BN == 0.
@@ -166,11 +168,12 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
   const int Gs = gridDim.x;
   const bool by_xcd = (Gs & 7) == 0 && mt_count >= 8;  // else: plain round-robin over tiles
   const int xcd = blockIdx.x & 7;
-  const int p_lo = by_xcd ? (int)(((long long)xcd * mt_count) >> 3) : 0;
-  const int p_hi = by_xcd ? (int)(((long long)(xcd + 1) * mt_count) >> 3) : mt_count;
+  const long long all_tiles = (long long)mt_count * nt_count;
+  const int t_lo = by_xcd ? (int)((xcd * all_tiles) >> 3) : 0;
+  const int t_hi = by_xcd ? (int)(((xcd + 1) * all_tiles) >> 3) : (int)all_tiles;
   const int slot0 = by_xcd ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   const int per = by_xcd ? (Gs >> 3) : Gs;
-  const int x_tiles = (p_hi - p_lo) * nt_count;
+  const int x_tiles = t_hi - t_lo;
   auto tile_of = [&](int k, int& panel, int& col) __attribute__((always_inline)) {
     const int u = slot0 + k * per;
     if (u >= x_tiles) {
@@ -178,11 +181,12 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
       col = 0;
       return;
     }
-    const int grp8 = u / (8 * nt_count);
-    const int v = u - grp8 * 8 * nt_count;
-    const int gp = min(8, p_hi - p_lo - grp8 * 8);
+    const int g = t_lo + u;
+    const int grp8 = g / (8 * nt_count);
+    const int v = g - grp8 * 8 * nt_count;
+    const int gp = min(8, mt_count - grp8 * 8);
     col = v / gp;
-    panel = p_lo + grp8 * 8 + (v - col * gp);
+    panel = grp8 * 8 + (v - col * gp);
   };
 
   auto stage_a = [&](int st) { return (GS_LDS bf16*)&smem[st * STAGE]; };
@@ -409,48 +413,64 @@ static int pp_persistent_grid(int tiles) {
   return tiles < g_pp_cus ? tiles : g_pp_cus;
 }
 
-hipError_t launch_qkv_proj_bf16_pp(const void* x, const void* wqkv, void* qkv, int M, int d,
-                                   hipStream_t stream) {
-  // 3d = 384 * heads is a multiple of 256 for an even head count
-  const int Nc = 3 * d;
+// Load balance: when the 256 x 256 tiles leave a partial last round and the
+// panels (256-row strips) that fill the whole rounds fill them exactly, those
+// panels run first and the remaining ones follow as a second launch of
+// 256 x 128 tiles, provided these fit one round.  Returns the first row of
+// the second part (M when one launch is kept).  For M = 55093 on 256 CUs,
+// out_proj (4 tiles per panel) runs 192 panels in 3 rounds and 24 panels as
+// 192 half tiles instead of 4 rounds for 3.4 rounds of work.  qkv_proj
+// (12 tiles per panel) keeps one launch: its 10.1 rounds leave a last round
+// of 32 tiles, which run faster than a full round (less contention for L2
+// and memory), and a split there (213 panels, then 3 as half tiles) measured
+// no faster.
+static int pp_split_rows(int M, int tiles_per_panel) {
   const int mt = (M + pp::BM - 1) / pp::BM;
-  hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, false, 2>), dim3(pp_persistent_grid(mt * (Nc / 256))),
-                     dim3(pp::THREADS), 0, stream, (const bf16*)x, (const bf16*)wqkv,
-                     (const bf16*)nullptr, (bf16*)qkv, M, Nc, d);
-  return hipGetLastError();
+  const int cus = pp_persistent_grid(1 << 30);
+  const long long tiles = (long long)mt * tiles_per_panel;
+  const int rounds = (int)(tiles / cus);
+  if (rounds < 1 || ((long long)rounds * cus) % tiles_per_panel != 0) return M;
+  const int main_panels = (int)((long long)rounds * cus / tiles_per_panel);
+  const int rest = mt - main_panels;
+  if (rest <= 0 || rest * 2 * tiles_per_panel > cus) return M;
+  return main_panels * pp::BM;
 }
 
-// Load balance: when the 256 x 256 tiles leave a partial last round that
-// 256 x 128 tiles can finish in one round, the rows of the whole rounds run
-// first and the remaining panels follow as a second launch of half-width
-// tiles (for d = 1024 on 256 CUs: 192 panels in 3 rounds, then 24 panels as
-// 192 tiles, instead of 4 rounds for 3.4 rounds of work).
-hipError_t launch_out_proj_bf16_pp(const void* o, const void* wo, const void* x, void* out, int M,
-                                   int d, hipStream_t stream) {
-  const int mt = (M + pp::BM - 1) / pp::BM;
-  const int nt = d / 256;
-  const int cus = pp_persistent_grid(1 << 30);
-  int main_panels = mt;
-  if (mt * nt > cus && cus % nt == 0) {
-    const int per_round = cus / nt;  // panels per round of 256 x 256 tiles
-    const int rounds = mt / per_round;
-    const int rest = mt - rounds * per_round;
-    if (rounds >= 1 && rest > 0 && rest * 2 * nt <= cus) main_panels = rounds * per_round;
-  }
-  const int m1 = min(M, main_panels * pp::BM);
-  hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, true, 2>), dim3(pp_persistent_grid(main_panels * nt)),
-                     dim3(pp::THREADS), 0, stream, (const bf16*)o, (const bf16*)wo, (const bf16*)x,
-                     (bf16*)out, m1, d, d);
+// C[r0 .. r0+rows) for one part of the row split (RESID: out_proj).
+template <int BN, bool RESID>
+static void pp_launch_part(const bf16* A, const bf16* W, const bf16* R, bf16* C, int r0, int rows,
+                           int Nc, int K, hipStream_t stream) {
+  const int mt = (rows + pp::BM - 1) / pp::BM;
+  const size_t a_off = (size_t)r0 * K, c_off = (size_t)r0 * Nc;
+  hipLaunchKernelGGL((gemm_pp_bf16_kernel<BN, RESID, 2>), dim3(pp_persistent_grid(mt * (Nc / BN))),
+                     dim3(pp::THREADS), 0, stream, A + a_off, W, RESID ? R + c_off : R, C + c_off,
+                     rows, Nc, K);
+}
+
+template <bool RESID>
+static hipError_t pp_launch(const bf16* A, const bf16* W, const bf16* R, bf16* C, int M, int Nc,
+                            int K, hipStream_t stream) {
+  const int m1 = pp_split_rows(M, Nc / 256);
+  pp_launch_part<256, RESID>(A, W, R, C, 0, m1, Nc, K, stream);
   if (m1 < M) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t off = (size_t)m1 * d;
-    hipLaunchKernelGGL((gemm_pp_bf16_kernel<128, true, 2>),
-                       dim3(pp_persistent_grid((mt - main_panels) * 2 * nt)), dim3(pp::THREADS), 0, stream,
-                       (const bf16*)o + off, (const bf16*)wo, (const bf16*)x + off, (bf16*)out + off, M - m1,
-                       d, d);
+    pp_launch_part<128, RESID>(A, W, R, C, m1, M - m1, Nc, K, stream);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_qkv_proj_bf16_pp(const void* x, const void* wqkv, void* qkv, int M, int d,
+                                   hipStream_t stream) {
+  // 3d = 384 * heads is a multiple of 256 for an even head count
+  return pp_launch<false>((const bf16*)x, (const bf16*)wqkv, nullptr, (bf16*)qkv, M, 3 * d, d,
+                          stream);
+}
+
+hipError_t launch_out_proj_bf16_pp(const void* o, const void* wo, const void* x, void* out, int M,
+                                   int d, hipStream_t stream) {
+  return pp_launch<true>((const bf16*)o, (const bf16*)wo, (const bf16*)x, (bf16*)out, M, d, d,
+                         stream);
 }
 
 }  // namespace gs
