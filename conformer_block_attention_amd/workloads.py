@@ -94,7 +94,14 @@ def draw_lengths(w: Workload) -> np.ndarray:
     raise ValueError(f"unknown length kind {w.length_kind!r}")
 
 
-# The five workloads, in the order the headline configurations are listed.
+# The five workloads, in the order the headline configurations are listed,
+# then bf16_b32_long_full: the long-clip batch with one block per sequence
+# (block_frames above every length), i.e. full bidirectional attention over
+# each packed sequence.  The pages run packed, non-causal attention for the
+# bidirectional editor (IBM model card, "Usage", installation note on the
+# attention backend; "Model Architecture" (3) Bidirectional LLM Editor); its
+# widths are not given, so the encoder's d = 1024, 8 heads are kept, with the
+# lengths of the multi-clip range.
 WORKLOADS = {
     "fp32_t422": Workload("fp32_t422", "fp32", "fixed", 1, fixed_length=422),
     "bf16_t800": Workload("bf16_t800", "bf16", "fixed", 1, fixed_length=800),
@@ -103,6 +110,8 @@ WORKLOADS = {
                                     lo=100, hi=1750, mean=425.0, sigma=0.35),
     "bf16_b128_chain16": Workload("bf16_b128_chain16", "bf16", "lognormal", 128,
                                   lo=100, hi=1750, mean=425.0, sigma=0.35, layers=16),
+    "bf16_b32_long_full": Workload("bf16_b32_long_full", "bf16", "uniform", 32, lo=1950, hi=4700,
+                                   block_frames=4700),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 HEADLINE = "bf16_b128_lognormal"

@@ -238,6 +238,45 @@ def test_workload_full_size_sampled(orc, name):
         assert torch.equal(one, out[a:b]), f"sequence {s} differs when run alone"
 
 
+def test_full_sequence_attention_sampled(orc):
+    """One block per sequence (block length above every length): full
+    bidirectional attention over each packed sequence of the long-clip batch,
+    32 sequences of 1950..4700 frames, in the launch configuration of the
+    benchmark.  The oracle computes sampled query rows of three sequences:
+    both ends, both sides of every 224-row query-group boundary, random rows.
+    The same call with a larger block length gives the same bits, and a
+    sequence run alone gives the bits it gets packed."""
+    name = "bf16_b32_long_full"
+    case = workloads.build_case(workloads.WORKLOADS[name])
+    G.print_case(name, frames=case.n_frames, block_frames=case.block_frames)
+    assert case.block_frames >= int(case.lengths.max())
+    x, cu, wqkv, wo = G.on_dev(case)
+    out = G.run(x, cu, wqkv, wo, case.block_frames, case.heads)
+    rng = np.random.default_rng(3)
+    mask = np.zeros(case.n_frames, np.uint8)
+    seqs = (0, len(case.lengths) // 2, len(case.lengths) - 1)
+    for s in seqs:
+        a, L = int(case.cu[s]), int(case.lengths[s])
+        rows = {0, 1, L - 2, L - 1}
+        for g in range(224, L, 224):
+            rows.update((g - 1, g))
+        rows.update(int(r) for r in rng.choice(L, size=32, replace=False))
+        mask[[a + r for r in rows]] = 1
+    ref = orc.block_mhsa(case.x, case.cu, case.weights[0][0], case.weights[0][1],
+                         case.block_frames, case.heads, mask=mask)
+    sel = mask.astype(bool)
+    err = G.rel_err(out.double().cpu().numpy()[sel], ref[sel])
+    print(f"  sampled rows={int(sel.sum())} err={err:.3e}", flush=True)
+    assert err <= G.BF16_TOL, err
+    wide = G.run(x, cu, wqkv, wo, 1 << 20, case.heads)
+    assert torch.equal(out, wide), "a larger block length changed the result"
+    for s in seqs:
+        a, b = int(case.cu[s]), int(case.cu[s + 1])
+        one = G.run(x[a:b].contiguous(), torch.tensor([0, b - a], dtype=torch.int32, device=G.dev()),
+                    wqkv, wo, case.block_frames, case.heads)
+        assert torch.equal(one, out[a:b]), f"sequence {s} differs when run alone"
+
+
 def test_workload_chain16_teacher_forced(orc):
     """16 layers with independent weights, each fed the previous layer's GPU output.
 
