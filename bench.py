@@ -47,17 +47,21 @@ def source_hash(kernel: str) -> str:
 
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs of this
-    workload, if the kernel's sources are still those that were measured."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
-    if not os.path.exists(p):
-        return None
-    with open(p) as f:
-        t = json.load(f)
-    if t.get("source_hash") != source_hash(kernel):
-        return None
-    if t.get("workload", "").split(" ")[0] != workload:
-        return None
-    return t.get("bytes_per_launch")
+    workload (profiles/traffic_<kernel>.json for the headline batch,
+    traffic_<kernel>.<workload>.json for others), if the kernel's sources are
+    still those that were measured."""
+    for name in (f"traffic_{kernel}.{workload}.json", f"traffic_{kernel}.json"):
+        p = os.path.join(ROOT, "profiles", name)
+        if not os.path.exists(p):
+            continue
+        with open(p) as f:
+            t = json.load(f)
+        if t.get("workload", "").split(" ")[0] != workload:
+            continue
+        if t.get("source_hash") != source_hash(kernel):
+            return None
+        return t.get("bytes_per_launch")
+    return None
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
