@@ -76,12 +76,19 @@ def cpu_baseline(case, budget_s: float = 12.0):
     frames = 0
     seqs = 0
     t0 = time.perf_counter()
+    t = case.bucket_frames
     for s in range(len(case.lengths)):
-        a, b = int(case.cu[s]), int(case.cu[s + 1])
-        xs = case.x[a:b].double().numpy()
-        orc.block_mhsa(xs, np.array([0, b - a], np.int32), w1, w2, case.block_frames, case.heads,
-                       nthreads=nthreads)
-        frames += b - a
+        if t:  # one padded bucket
+            xs = case.x[s * t:(s + 1) * t].double().numpy()
+            orc.block_mhsa_padded(xs, case.lengths[s:s + 1], t, w1, w2, case.block_frames,
+                                  case.heads, nthreads=nthreads)
+            frames += int(case.lengths[s])
+        else:
+            a, b = int(case.cu[s]), int(case.cu[s + 1])
+            xs = case.x[a:b].double().numpy()
+            orc.block_mhsa(xs, np.array([0, b - a], np.int32), w1, w2, case.block_frames,
+                           case.heads, nthreads=nthreads)
+            frames += b - a
         seqs += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -136,13 +143,21 @@ def main():
     bufs = [torch.empty_like(x), torch.empty_like(x)]
     stream = torch.cuda.current_stream()
 
+    t = case.bucket_frames
+    lens = torch.from_numpy(case.lengths.astype(np.int32)).to(dev)
+
     def step(events=None, ev_base=0):
         cur = x
         for l, (wqkv, wo) in enumerate(weights):
             o = bufs[l & 1]
-            gsattn.block_mhsa_fwd(cur, cu, wqkv, wo, case.block_frames, case.heads, out=o,
-                                  workspace=ws, stream=stream,
-                                  kernel_events=events.view(ev_base + 4 * l) if events else None)
+            kev = events.view(ev_base + 4 * l) if events else None
+            if t:
+                gsattn.block_mhsa_fwd_padded(cur.view(-1, t, d), lens, wqkv, wo, case.block_frames,
+                                             case.heads, out=o.view(-1, t, d), workspace=ws,
+                                             stream=stream, kernel_events=kev)
+            else:
+                gsattn.block_mhsa_fwd(cur, cu, wqkv, wo, case.block_frames, case.heads, out=o,
+                                      workspace=ws, stream=stream, kernel_events=kev)
             cur = o
         return cur
 
@@ -167,13 +182,16 @@ def main():
     avg_ms = {k: float(np.mean(v)) for k, v in per.items()}
 
     ms_step = el / args.steps * 1e3
-    frames_per_s = n * nl / (el / args.steps)  # frame-layers per second
+    valid = int(np.sum(case.lengths))  # frames (padding rows excluded)
+    frames_per_s = valid * nl / (el / args.steps)  # frame-layers per second
     fl = accounting.useful_flops(case.lengths, d, case.block_frames)
     tflops = fl["total"] * nl / (el / args.steps) / 1e12
     bf16 = x.dtype == torch.bfloat16
     peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
     elem = 2 if bf16 else 4
-    by = accounting.algorithmic_bytes(n, d, elem)
+    by = accounting.algorithmic_bytes(n, d, elem)  # all rows the projections touch
+    if t:  # padded: attention reads Q|K|V of the valid rows and writes O for every row
+        by["block_attn"] = elem * (3 * valid * d + n * d)
 
     # dominant kernel and its roofline: the bound is whichever of its useful
     # flops at the matrix peak and its algorithmic bytes at the HBM peak takes
@@ -211,7 +229,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "global_batch": int(len(case.lengths)), "frames": int(n),
+        "config": {"workload": w.name, "global_batch": int(len(case.lengths)), "frames": valid,
+                   "rows": int(n), "bucket_frames": t or None,
                    "blocks": len(accounting.block_table(case.lengths, case.block_frames)),
                    "block_frames": case.block_frames, "d_model": int(d), "heads": case.heads,
                    "layers": nl, "seed": w.seed},

@@ -805,7 +805,7 @@ static int g_num_cus = 0;
 
 int attn_bf16_table_entries(long long N) { return (int)(N + 1); }
 
-hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long long N, int d,
+hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long N, int d,
                                   int heads, int B, void* o, void* table, hipStream_t stream) {
   if (g_num_cus == 0) {
     int dev = 0, n = 0;
@@ -817,7 +817,7 @@ hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long lo
   // workspace: the unit table, then (256-byte aligned) one flag word per unit
   unsigned long long* ovf =
       (unsigned long long*)((char*)table + ((16 * (N + 1) + 255) / 256) * 256);
-  build_unit_table_kernel<ATT_QG, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(cu, S, B, (int4*)table,
+  build_unit_table_kernel<ATT_QG, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(sp, S, B, (int4*)table,
                                                                                      ovf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

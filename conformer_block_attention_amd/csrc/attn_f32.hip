@@ -19,13 +19,13 @@ constexpr int AF_DH = 128;
 constexpr int AF_LD = AF_DH + 4;   // padded LDS row (floats)
 
 __global__ __launch_bounds__(AF_THREADS) void block_attn_f32_kernel(
-    const float* __restrict__ qkv, const int* __restrict__ cu, int S, int B, int d,
-    float scale_log2, float* __restrict__ O) {
+    const float* __restrict__ qkv, SeqSpans sp, int S, int B, int d, float scale_log2,
+    float* __restrict__ O) {
   __shared__ float Ks[AF_KC * AF_LD];
   __shared__ float Vs[AF_KC * AF_LD];
 
   AttnUnit U;
-  if (!find_unit<AF_QG>(cu, S, B, blockIdx.x, U)) return;
+  if (!find_unit<AF_QG>(sp, S, B, blockIdx.x, U)) return;
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4;
@@ -124,12 +124,12 @@ __global__ __launch_bounds__(AF_THREADS) void block_attn_f32_kernel(
                                            oacc[dt][2] * inv, oacc[dt][3] * inv);
 }
 
-hipError_t launch_block_attn_f32(const void* qkv, const int* cu, int S, long long N, int d,
+hipError_t launch_block_attn_f32(const void* qkv, SeqSpans sp, int S, long long N, int d,
                                  int heads, int B, void* o, hipStream_t stream) {
   const int units = attn_unit_bound(N, S, B, AF_QG);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)AF_DH);
   hipLaunchKernelGGL(block_attn_f32_kernel, dim3(units, heads), dim3(AF_THREADS), 0, stream,
-                     (const float*)qkv, cu, S, B, d, scale_log2, (float*)o);
+                     (const float*)qkv, sp, S, B, d, scale_log2, (float*)o);
   return hipGetLastError();
 }
 

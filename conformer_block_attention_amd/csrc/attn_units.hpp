@@ -1,15 +1,29 @@
 // attn_units.hpp -- work units of the block-attention kernels.
 //
 // A block is a run of at most B consecutive rows of one sequence; blocks
-// restart at every cu_seqlens boundary and the last block of a sequence holds
-// the remainder.  A work unit is one block, or a group of at most QG query rows
+// restart at every sequence start and the last block of a sequence holds the
+// remainder.  A work unit is one block, or a group of at most QG query rows
 // of a block when B > QG.  Units are numbered sequence by sequence, block by
-// block, and are located on the device from cu_seqlens alone.
+// block, and are located on the device from the sequence spans alone.
 #pragma once
 
 #include "gs_device.hpp"
 
 namespace gs {
+
+// Where sequence s lives: packed (rows cu[s] .. cu[s+1]-1 of a cu_seqlens
+// array) or padded (rows s*T .. s*T + len[s] - 1 of fixed buckets of T rows,
+// the rest of the bucket being padding; a length outside [0, T] is clamped).
+struct SeqSpans {
+  const int* p;  // cu_seqlens [S+1] (stride 0) or lengths [S] (stride T > 0)
+  int stride;
+  __device__ __forceinline__ int start(int s) const { return stride ? s * stride : p[s]; }
+  __device__ __forceinline__ int len(int s) const {
+    if (!stride) return p[s + 1] - p[s];
+    const int l = p[s];
+    return l < 0 ? 0 : (l > stride ? stride : l);
+  }
+};
 
 struct AttnUnit {
   int row0;   // first row of the block
@@ -31,14 +45,14 @@ __device__ __forceinline__ int units_of_seq(int len, int B, int upb) {
 // Wave-level search for unit u (every lane gets the result).  Sequences are
 // scanned 64 at a time with a wave prefix sum.  False if u is past the end.
 template <int QG>
-__device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnUnit& out) {
+__device__ bool find_unit(SeqSpans sp, int S, int B, int u, AttnUnit& out) {
   const int lane = threadIdx.x & 63;
   const int upb = (B - 1) / QG + 1;
   int base = 0;
   for (int c0 = 0; c0 < S; c0 += 64) {
     const int s = c0 + lane;
     int len = 0;
-    if (s < S) len = cu[s + 1] - cu[s];
+    if (s < S) len = sp.len(s);
     const int units = units_of_seq<QG>(len, B, upb);
     int incl = units;
 #pragma unroll
@@ -58,7 +72,7 @@ __device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnU
       int j = v / upb;
       if (j > nb - 1) j = nb - 1;
       const int g = v - j * upb;
-      out.row0 = cu[seq] + j * B;
+      out.row0 = sp.start(seq) + j * B;
       out.L = (j < nb - 1) ? B : slen - (nb - 1) * B;
       out.q0 = g * QG;
       out.qn = min(QG, out.L - out.q0);
@@ -83,8 +97,8 @@ __device__ bool find_unit(const int* __restrict__ cu, int S, int B, int u, AttnU
 // One workgroup; a counting sort over the cost: a histogram pass and a
 // placement pass over the sequences, 1024 sequences at a time.
 template <int QG, int KC>
-__global__ __launch_bounds__(1024) void build_unit_table_kernel(const int* __restrict__ cu, int S,
-                                                               int B, int4* __restrict__ table,
+__global__ __launch_bounds__(1024) void build_unit_table_kernel(SeqSpans sp, int S, int B,
+                                                               int4* __restrict__ table,
                                                                unsigned long long* __restrict__ flags) {
   constexpr int BINS = 1024;
   __shared__ int next[BINS];  // per cost bin: count, then next free position
@@ -110,10 +124,10 @@ __global__ __launch_bounds__(1024) void build_unit_table_kernel(const int* __res
     for (int c0 = 0; c0 < S; c0 += 1024) {
       const int s = c0 + tid;
       int len = 0;
-      if (s < S) len = cu[s + 1] - cu[s];
+      if (s < S) len = sp.len(s);
       const int n = units_of_seq<QG>(len, B, upb);
       if (n > 0) {
-        const int start = cu[s];
+        const int start = sp.start(s);
         for (int v = 0; v < n; ++v) {
           const int4 e = unit(start, len, v);
           const int pos = atomicAdd(&next[bin_of(e)], 1);

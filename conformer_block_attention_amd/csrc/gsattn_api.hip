@@ -19,13 +19,13 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int 
                                 hipStream_t stream);
 hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
                                 int d, hipStream_t stream);
-hipError_t launch_block_attn_bf16(const void* qkv, const int* cu, int S, long long N, int d,
+hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long N, int d,
                                   int heads, int B, void* o, void* table, hipStream_t stream);
 hipError_t launch_qkv_proj_f32(const void* x, const void* wqkv, void* qkv, int M, int d,
                                hipStream_t stream);
 hipError_t launch_out_proj_f32(const void* o, const void* wo, const void* x, void* out, int M,
                                int d, hipStream_t stream);
-hipError_t launch_block_attn_f32(const void* qkv, const int* cu, int S, long long N, int d,
+hipError_t launch_block_attn_f32(const void* qkv, SeqSpans sp, int S, long long N, int d,
                                  int heads, int B, void* o, hipStream_t stream);
 
 // Validates cu_seqlens on the device: flag[0] = 0 if cu[0] == 0, cu is
@@ -38,6 +38,34 @@ __global__ void check_cu_kernel(const int* cu, int S, long long N, int* flag) {
     if (cu[s + 1] < cu[s]) atomicOr(&bad, 1);
   __syncthreads();
   if (threadIdx.x == 0) flag[0] = bad;
+}
+
+// Validates padded lengths: flag[0] = 1 if some len[s] is outside [0, T].
+__global__ void check_lengths_kernel(const int* len, int S, int T, int* flag) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += blockDim.x)
+    if (len[s] < 0 || len[s] > T) atomicOr(&bad, 1);
+  __syncthreads();
+  if (threadIdx.x == 0) flag[0] = bad;
+}
+
+// Zeroes the padding rows len[b] .. T-1 of every bucket b of o [S*T][d]
+// (their attention output), ZP_ROWS rows of a bucket per workgroup, in
+// 16-byte pieces: grid (ceil(T / ZP_ROWS), S).
+constexpr int ZP_ROWS = 16;
+__global__ __launch_bounds__(256) void zero_pad_rows_kernel(const int* len, int T, int pieces,
+                                                            uint4* o) {
+  const int b = blockIdx.y;
+  int l = len[b];
+  l = l < 0 ? 0 : (l > T ? T : l);
+  const int t0 = blockIdx.x * ZP_ROWS;
+  const int t1 = min(t0 + ZP_ROWS, T);
+  for (int t = max(t0, l); t < t1; ++t) {
+    uint4* row = o + ((size_t)b * T + t) * pieces;
+    for (int i = threadIdx.x; i < pieces; i += blockDim.x) row[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 }  // namespace gs
 
@@ -127,6 +155,83 @@ gs_status debug_check_cu(const int32_t* cu, int32_t S, int64_t N, int* dflag, hi
   return GS_OK;
 }
 
+gs_status debug_check_lengths(const int32_t* len, int32_t S, int32_t T, int* dflag,
+                              hipStream_t st) {
+  if (!debug_checks()) return GS_OK;
+  hipLaunchKernelGGL(gs::check_lengths_kernel, dim3(1), dim3(256), 0, st, (const int*)len, (int)S,
+                     (int)T, dflag);
+  GS_TRY(hip_status(hipGetLastError(), "lengths check launch"));
+  int flag = 1;
+  GS_TRY(hip_status(hipMemcpyAsync(&flag, dflag, sizeof(int), hipMemcpyDeviceToHost, st),
+                    "lengths check copy"));
+  GS_TRY(hip_status(hipStreamSynchronize(st), "lengths check sync"));
+  if (flag) return fail(GS_ERR_INVALID_ARGUMENT, "a length is outside [0, bucket_frames]");
+  return GS_OK;
+}
+
+// The attention step over sequences given as spans (packed or padded).
+gs_status attn_spans(const void* qkv, gs::SeqSpans sp, int32_t S, int64_t N, int32_t d,
+                     int32_t heads, int32_t B, gs_dtype dtype, void* o, void* table,
+                     hipStream_t stream) {
+  hipError_t e = dtype == GS_BF16
+                     ? gs::launch_block_attn_bf16(qkv, sp, S, N, d, heads, B, o, table, stream)
+                     : gs::launch_block_attn_f32(qkv, sp, S, N, d, heads, B, o, stream);
+  return hip_status(e, "block_attn launch");
+}
+
+// Checks shared by the whole-sub-layer entry points; on success the
+// workspace pieces are set.
+struct FwdPlan {
+  int64_t N;
+  int32_t d;
+  void* qkv;
+  void* o;
+  char* table;
+  size_t table_bytes;
+  int* dflag;
+};
+
+gs_status plan_fwd(const void* x, const void* Wqkv, const void* Wo, int32_t block_frames,
+                   int32_t heads, void* out, const gs_mhsa_desc* desc, FwdPlan& p) {
+  if (!desc) return fail(GS_ERR_INVALID_ARGUMENT, "desc is NULL");
+  GS_TRY(check_dtype(desc->dtype));
+  const int64_t N = desc->total_frames;
+  const int32_t d = desc->d_model;
+  GS_TRY(check_dims(N, d));
+  GS_TRY(check_heads(d, heads));
+  if (desc->num_seqs < 1) return fail(GS_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", desc->num_seqs);
+  if (block_frames < 1) return fail(GS_ERR_INVALID_ARGUMENT, "block_frames %d < 1", block_frames);
+  p.N = N;
+  p.d = d;
+  if (N == 0) return GS_OK;
+  GS_TRY(check_ptr(x, "x"));
+  GS_TRY(check_ptr(Wqkv, "Wqkv"));
+  GS_TRY(check_ptr(Wo, "Wo"));
+  GS_TRY(check_ptr(out, "out"));
+  const size_t e = elem_size(desc->dtype);
+  const size_t xbytes = (size_t)N * d * e;
+  if (out != x) {
+    const char* a = (const char*)x;
+    const char* b = (const char*)out;
+    if (a < b + xbytes && b < a + xbytes)
+      return fail(GS_ERR_INVALID_ARGUMENT, "out partially overlaps x");
+  }
+  const size_t need = gs_block_mhsa_workspace_bytes(N, d, desc->dtype);
+  if (!desc->workspace) return fail(GS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (((uintptr_t)desc->workspace & (kAlign - 1)) != 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (desc->workspace_bytes < need)
+    return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                desc->workspace_bytes, need);
+  char* ws = (char*)desc->workspace;
+  p.qkv = ws;
+  p.o = ws + align_up((size_t)N * 3 * d * e);
+  p.table = (char*)p.o + align_up((size_t)N * d * e);
+  p.table_bytes = gs_block_attn_workspace_bytes(N);
+  p.dflag = (int*)(p.table + p.table_bytes);
+  return GS_OK;
+}
+
 gs_status record(const gs_mhsa_desc* desc, int i, hipStream_t st) {
   if (!desc->kernel_events) return GS_OK;
   return hip_status(hipEventRecord(desc->kernel_events[i], st), "hipEventRecord");
@@ -200,13 +305,8 @@ gs_status gs_block_attn(const void* qkv, const int32_t* cu_seqlens, int32_t num_
   const size_t need = gs_block_attn_workspace_bytes(total_frames);
   if (workspace_bytes < need)
     return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  const long long N = total_frames;
-  hipError_t e =
-      dtype == GS_BF16
-          ? gs::launch_block_attn_bf16(qkv, cu_seqlens, num_seqs, N, d_model, heads, block_frames, o,
-                                       workspace, stream)
-          : gs::launch_block_attn_f32(qkv, cu_seqlens, num_seqs, N, d_model, heads, block_frames, o, stream);
-  return hip_status(e, "block_attn launch");
+  return attn_spans(qkv, gs::SeqSpans{cu_seqlens, 0}, num_seqs, total_frames, d_model, heads,
+                    block_frames, dtype, o, workspace, stream);
 }
 
 gs_status gs_out_proj_residual(const void* o, const void* Wo, const void* x, void* out,
@@ -228,51 +328,50 @@ gs_status gs_out_proj_residual(const void* o, const void* Wo, const void* x, voi
 gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void* Wqkv,
                             const void* Wo, int32_t block_frames, int32_t heads, void* out,
                             hipStream_t stream, const gs_mhsa_desc* desc) {
-  if (!desc) return fail(GS_ERR_INVALID_ARGUMENT, "desc is NULL");
-  GS_TRY(check_dtype(desc->dtype));
-  const int64_t N = desc->total_frames;
-  const int32_t d = desc->d_model;
-  GS_TRY(check_dims(N, d));
-  GS_TRY(check_heads(d, heads));
-  if (desc->num_seqs < 1) return fail(GS_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", desc->num_seqs);
-  if (block_frames < 1) return fail(GS_ERR_INVALID_ARGUMENT, "block_frames %d < 1", block_frames);
+  FwdPlan p{};
+  GS_TRY(plan_fwd(x, Wqkv, Wo, block_frames, heads, out, desc, p));
   if (!cu_seqlens) return fail(GS_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
-  if (N == 0) return GS_OK;
-  GS_TRY(check_ptr(x, "x"));
-  GS_TRY(check_ptr(Wqkv, "Wqkv"));
-  GS_TRY(check_ptr(Wo, "Wo"));
-  GS_TRY(check_ptr(out, "out"));
-  const size_t e = elem_size(desc->dtype);
-  const size_t xbytes = (size_t)N * d * e;
-  if (out != x) {
-    const char* a = (const char*)x;
-    const char* b = (const char*)out;
-    if (a < b + xbytes && b < a + xbytes)
-      return fail(GS_ERR_INVALID_ARGUMENT, "out partially overlaps x");
-  }
-  const size_t need = gs_block_mhsa_workspace_bytes(N, d, desc->dtype);
-  if (!desc->workspace) return fail(GS_ERR_INVALID_ARGUMENT, "workspace is NULL");
-  if (((uintptr_t)desc->workspace & (kAlign - 1)) != 0)
-    return fail(GS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-  if (desc->workspace_bytes < need)
-    return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
-                desc->workspace_bytes, need);
-
-  char* ws = (char*)desc->workspace;
-  void* qkv = ws;
-  void* o = ws + align_up((size_t)N * 3 * d * e);
-  char* table = (char*)o + align_up((size_t)N * d * e);
-  const size_t table_bytes = gs_block_attn_workspace_bytes(N);
-  int* dflag = (int*)(table + table_bytes);
-  GS_TRY(debug_check_cu(cu_seqlens, desc->num_seqs, N, dflag, stream));
+  if (p.N == 0) return GS_OK;
+  GS_TRY(debug_check_cu(cu_seqlens, desc->num_seqs, p.N, p.dflag, stream));
 
   GS_TRY(record(desc, 0, stream));
-  GS_TRY(gs_qkv_proj(x, Wqkv, qkv, N, d, desc->dtype, stream));
+  GS_TRY(gs_qkv_proj(x, Wqkv, p.qkv, p.N, p.d, desc->dtype, stream));
   GS_TRY(record(desc, 1, stream));
-  GS_TRY(gs_block_attn(qkv, cu_seqlens, desc->num_seqs, N, d, heads, block_frames, desc->dtype, o,
-                       table, table_bytes, stream));
+  GS_TRY(gs_block_attn(p.qkv, cu_seqlens, desc->num_seqs, p.N, p.d, heads, block_frames,
+                       desc->dtype, p.o, p.table, p.table_bytes, stream));
   GS_TRY(record(desc, 2, stream));
-  GS_TRY(gs_out_proj_residual(o, Wo, x, out, N, d, desc->dtype, stream));
+  GS_TRY(gs_out_proj_residual(p.o, Wo, x, out, p.N, p.d, desc->dtype, stream));
+  GS_TRY(record(desc, 3, stream));
+  return GS_OK;
+}
+
+gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_t bucket_frames,
+                                   const void* Wqkv, const void* Wo, int32_t block_frames,
+                                   int32_t heads, void* out, hipStream_t stream,
+                                   const gs_mhsa_desc* desc) {
+  FwdPlan p{};
+  GS_TRY(plan_fwd(x, Wqkv, Wo, block_frames, heads, out, desc, p));
+  if (!lengths) return fail(GS_ERR_INVALID_ARGUMENT, "lengths is NULL");
+  if (bucket_frames < 1) return fail(GS_ERR_INVALID_ARGUMENT, "bucket_frames %d < 1", bucket_frames);
+  if ((int64_t)desc->num_seqs * bucket_frames != p.N)
+    return fail(GS_ERR_INVALID_ARGUMENT, "total_frames %lld != num_seqs %d * bucket_frames %d",
+                (long long)p.N, desc->num_seqs, bucket_frames);
+  if (p.N == 0) return GS_OK;
+  GS_TRY(debug_check_lengths(lengths, desc->num_seqs, bucket_frames, p.dflag, stream));
+  const size_t e = elem_size(desc->dtype);
+
+  GS_TRY(record(desc, 0, stream));
+  GS_TRY(gs_qkv_proj(x, Wqkv, p.qkv, p.N, p.d, desc->dtype, stream));
+  GS_TRY(record(desc, 1, stream));
+  GS_TRY(attn_spans(p.qkv, gs::SeqSpans{lengths, bucket_frames}, desc->num_seqs, p.N, p.d, heads,
+                    block_frames, desc->dtype, p.o, p.table, stream));
+  hipLaunchKernelGGL(gs::zero_pad_rows_kernel,
+                     dim3((bucket_frames + gs::ZP_ROWS - 1) / gs::ZP_ROWS, desc->num_seqs),
+                     dim3(256), 0, stream, (const int*)lengths, (int)bucket_frames,
+                     (int)((size_t)p.d * e / 16), (uint4*)p.o);
+  GS_TRY(hip_status(hipGetLastError(), "padding rows launch"));
+  GS_TRY(record(desc, 2, stream));
+  GS_TRY(gs_out_proj_residual(p.o, Wo, x, out, p.N, p.d, desc->dtype, stream));
   GS_TRY(record(desc, 3, stream));
   return GS_OK;
 }

@@ -20,7 +20,8 @@ GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE_TOO_SMALL, 
 GS_F32, GS_BF16 = 0, 1
 
 EXPORTS = (
-    "gs_block_mhsa_workspace_bytes", "gs_block_mhsa_fwd", "gs_qkv_proj", "gs_block_attn",
+    "gs_block_mhsa_workspace_bytes", "gs_block_mhsa_fwd", "gs_block_mhsa_fwd_padded",
+    "gs_qkv_proj", "gs_block_attn",
     "gs_block_attn_workspace_bytes", "gs_out_proj_residual", "gs_status_string",
     "gs_last_error_detail", "gs_version",
 )
@@ -63,6 +64,9 @@ def load(path: Optional[str] = None):
     lib.gs_block_mhsa_workspace_bytes.argtypes = [I64, I32, ctypes.c_int]
     lib.gs_block_mhsa_fwd.restype = ctypes.c_int
     lib.gs_block_mhsa_fwd.argtypes = [P, P, P, P, I32, I32, P, P, ctypes.POINTER(_Desc)]
+    lib.gs_block_mhsa_fwd_padded.restype = ctypes.c_int
+    lib.gs_block_mhsa_fwd_padded.argtypes = [P, P, I32, P, P, I32, I32, P, P,
+                                             ctypes.POINTER(_Desc)]
     lib.gs_qkv_proj.restype = ctypes.c_int
     lib.gs_qkv_proj.argtypes = [P, P, P, I64, I32, ctypes.c_int, P]
     lib.gs_block_attn.restype = ctypes.c_int
@@ -140,6 +144,33 @@ def block_mhsa_fwd(x: torch.Tensor, cu_seqlens: torch.Tensor, wqkv: torch.Tensor
                  int(workspace.numel()), kernel_events.handle_array() if kernel_events else None)
     _check(lib.gs_block_mhsa_fwd(
         _dev(x, "x"), _dev(cu_seqlens, "cu_seqlens"), _dev(wqkv, "Wqkv", x.dtype),
+        _dev(wo, "Wo", x.dtype), int(block_frames), int(heads), _dev(out, "out", x.dtype),
+        _stream(stream), ctypes.byref(desc)))
+    return out
+
+
+def block_mhsa_fwd_padded(x: torch.Tensor, lengths: torch.Tensor, wqkv: torch.Tensor,
+                          wo: torch.Tensor, block_frames: int, heads: int,
+                          out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None,
+                          kernel_events: Optional["HipEvents"] = None) -> torch.Tensor:
+    """The sub-layer on padded buckets: x [S, T, d], lengths int32 [S] (valid
+    rows per bucket).  Padding rows come back equal to x."""
+    lib = load()
+    if x.dim() != 3:
+        raise ValueError("x must be [buckets, bucket_frames, d_model]")
+    s, t, d = x.shape
+    dt = _gs_dtype(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(s * t, d, x.dtype, x.device)
+    if lengths.dtype != torch.int32 or lengths.numel() != s:
+        raise TypeError("lengths must be int32 with one entry per bucket")
+    desc = _Desc(int(s), int(s * t), int(d), dt, workspace.data_ptr(), int(workspace.numel()),
+                 kernel_events.handle_array() if kernel_events else None)
+    _check(lib.gs_block_mhsa_fwd_padded(
+        _dev(x, "x"), _dev(lengths, "lengths"), int(t), _dev(wqkv, "Wqkv", x.dtype),
         _dev(wo, "Wo", x.dtype), int(block_frames), int(heads), _dev(out, "out", x.dtype),
         _stream(stream), ctypes.byref(desc)))
     return out

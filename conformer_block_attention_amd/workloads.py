@@ -69,13 +69,16 @@ class Workload:
     hi: int = 0
     mean: float = 0.0         # "lognormal": arithmetic mean of the unclipped draw
     sigma: float = 0.0        # "lognormal": log-space standard deviation
+    bucket_frames: int = 0    # > 0: padded layout, one bucket of this many rows per sequence
 
     @property
     def torch_dtype(self) -> torch.dtype:
         return torch.float32 if self.dtype == "fp32" else torch.bfloat16
 
     def lengths(self) -> np.ndarray:
-        return draw_lengths(self)
+        """Valid frames per sequence (for a padded layout, capped at the bucket)."""
+        ln = draw_lengths(self)
+        return np.minimum(ln, self.bucket_frames) if self.bucket_frames else ln
 
 
 def draw_lengths(w: Workload) -> np.ndarray:
@@ -101,7 +104,10 @@ def draw_lengths(w: Workload) -> np.ndarray:
 # bidirectional editor (IBM model card, "Usage", installation note on the
 # attention backend; "Model Architecture" (3) Bidirectional LLM Editor); its
 # widths are not given, so the encoder's d = 1024, 8 heads are kept, with the
-# lengths of the multi-clip range.
+# lengths of the multi-clip range.  bf16_bucket800_b128: the fixed-length
+# layout of the portable INT4 export (README "What Changed" item 4: a fixed
+# bucket of 800 encoder frames), 128 buckets of 800 rows whose valid lengths
+# are the headline batch's lengths capped at 800.
 WORKLOADS = {
     "fp32_t422": Workload("fp32_t422", "fp32", "fixed", 1, fixed_length=422),
     "bf16_t800": Workload("bf16_t800", "bf16", "fixed", 1, fixed_length=800),
@@ -112,6 +118,8 @@ WORKLOADS = {
                                   lo=100, hi=1750, mean=425.0, sigma=0.35, layers=16),
     "bf16_b32_long_full": Workload("bf16_b32_long_full", "bf16", "uniform", 32, lo=1950, hi=4700,
                                    block_frames=4700),
+    "bf16_bucket800_b128": Workload("bf16_bucket800_b128", "bf16", "lognormal", 128, lo=100,
+                                    hi=1750, mean=425.0, sigma=0.35, bucket_frames=800),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 HEADLINE = "bf16_b128_lognormal"
@@ -153,13 +161,14 @@ class Case:
     """Materialised inputs of one workload (CPU tensors)."""
 
     name: str
-    lengths: np.ndarray
-    cu: np.ndarray
-    x: torch.Tensor
+    lengths: np.ndarray      # valid frames per sequence
+    cu: np.ndarray           # prefix sums of `lengths` (for a packed layout: x's row offsets)
+    x: torch.Tensor          # [rows, d]: packed sequences, or len(lengths) buckets of bucket_frames rows
     weights: list            # [(Wqkv, Wo)] per layer
     block_frames: int
     heads: int
     dtype: torch.dtype
+    bucket_frames: int = 0   # > 0: padded layout
 
     @property
     def n_frames(self) -> int:
@@ -173,11 +182,12 @@ class Case:
 def build_case(w: Workload, layers: Optional[int] = None) -> Case:
     lengths = w.lengths()
     cu = cu_seqlens(lengths)
-    n = int(cu[-1])
+    n = len(lengths) * w.bucket_frames if w.bucket_frames else int(cu[-1])
     x = make_x(n, w.d_model, w.torch_dtype, w.seed)
     nl = w.layers if layers is None else layers
     weights = [make_weights(w.d_model, w.torch_dtype, w.seed, l) for l in range(nl)]
-    return Case(w.name, lengths, cu, x, weights, w.block_frames, w.heads, w.torch_dtype)
+    return Case(w.name, lengths, cu, x, weights, w.block_frames, w.heads, w.torch_dtype,
+                w.bucket_frames)
 
 
 def custom_case(lengths, d_model: int, heads: int, block_frames: int, dtype: torch.dtype,

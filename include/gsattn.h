@@ -102,6 +102,31 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
                             hipStream_t stream, const gs_mhsa_desc* desc);
 
 /*
+ * The whole sub-layer on fixed-length padded buckets instead of packed
+ * sequences (the fixed [1, 800, features] encoder bucket of the portable
+ * INT4 export, README "What Changed" item 4; how its padding is treated is
+ * not stated there, so this reading is used):
+ *   x        [S][T][d]  S buckets of T = bucket_frames rows; in bucket b the
+ *                       first lengths[b] rows are the sequence, the rest is
+ *                       padding (any finite values)
+ *   lengths  [S]        int32 valid rows per bucket, 0 <= lengths[b] <= T
+ *                       (device; values outside are clamped, or rejected
+ *                       under GSATTN_DEBUG_CHECKS=1)
+ *   bucket_frames       T >= 1; desc->num_seqs = S, desc->total_frames = S*T
+ *   Wqkv, Wo, block_frames, heads, out, stream: as gs_block_mhsa_fwd.
+ * Blocks restart at each bucket's first row and never include padding rows,
+ * so the valid rows of `out` equal those of gs_block_mhsa_fwd on the same
+ * sequences packed.  Padding rows are neither queries nor keys: their
+ * attention output is zero, so out = x there (up to the sign of zero).  The
+ * projections run over all S*T rows; the workspace is that of
+ * gs_block_mhsa_workspace_bytes(S*T, d, dtype).
+ */
+gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_t bucket_frames,
+                                   const void* Wqkv, const void* Wo, int32_t block_frames,
+                                   int32_t heads, void* out, hipStream_t stream,
+                                   const gs_mhsa_desc* desc);
+
+/*
  * Step 1 alone: qkv[N][3d] = x[N][d] . Wqkv[3d][d]^T (fp32 accumulate).
  */
 gs_status gs_qkv_proj(const void* x, const void* Wqkv, void* qkv, int64_t total_frames,

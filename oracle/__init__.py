@@ -154,6 +154,39 @@ class Oracle:
         return out
 
 
+    def block_mhsa_padded(self, x, lengths, bucket_frames: int, wqkv, wo, block_frames: int,
+                          heads: int, mask=None, nthreads=None) -> np.ndarray:
+        """The sub-layer on fixed-length padded buckets (the fixed 800-frame
+        encoder bucket of the portable INT4 export, README "What Changed"
+        item 4; the treatment of padding is a reading: padding rows are
+        neither queries nor keys, and their output is x).
+
+        x is [S*T, d] (or [S, T, d]); the first lengths[b] rows of bucket b
+        (clamped to [0, T]) are sequence b.  By that definition the valid rows,
+        taken bucket by bucket, are a packed batch whose offsets are the prefix
+        sums of the lengths: they are computed as such, and padding rows copy
+        x.  Rows outside `mask` (if given) among the valid ones come back as
+        NaN; padding rows always hold x."""
+        x = self._f64(x)
+        t = int(bucket_frames)
+        x = x.reshape(-1, x.shape[-1])
+        n, d = x.shape
+        lengths = np.asarray(lengths, np.int64)
+        if t < 1 or n != len(lengths) * t:
+            raise ValueError("x must hold len(lengths) buckets of bucket_frames rows")
+        ln = np.clip(lengths, 0, t)
+        idx = np.concatenate([b * t + np.arange(ln[b]) for b in range(len(ln))] +
+                             [np.zeros(0, np.int64)]).astype(np.int64)
+        out = x.copy()
+        if idx.size:
+            cu = np.zeros(len(ln) + 1, np.int32)
+            cu[1:] = np.cumsum(ln)
+            m = None if mask is None else np.asarray(mask, np.uint8).reshape(-1)[idx]
+            out[idx] = self.block_mhsa(np.ascontiguousarray(x[idx]), cu, wqkv, wo, block_frames,
+                                       heads, mask=m, nthreads=nthreads)
+        return out
+
+
 _default: Optional[Oracle] = None
 
 

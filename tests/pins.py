@@ -69,6 +69,33 @@ def brute_force(x, cu, wqkv, wo, block, heads):
     return x + o @ wo.T
 
 
+def brute_force_padded(x, lengths, bucket, wqkv, wo, block, heads):
+    """Padded buckets x [S*T, d] straight in the padded layout: full
+    (S*T) x (S*T) attention where a query may see a key only if both are
+    valid rows of the same bucket and the same block; padding rows get a
+    zero attention output."""
+    n, d = x.shape
+    dh = d // heads
+    qkv = x @ wqkv.T
+    row = np.arange(n)
+    bkt, pos = row // bucket, row % bucket
+    valid = pos < np.clip(np.asarray(lengths), 0, bucket)[bkt]
+    blk = pos // block
+    allowed = ((bkt[:, None] == bkt[None, :]) & (blk[:, None] == blk[None, :]) &
+               valid[:, None] & valid[None, :])
+    o = np.zeros((n, d))
+    for h in range(heads):
+        q = qkv[:, h * dh:(h + 1) * dh]
+        k = qkv[:, d + h * dh:d + (h + 1) * dh]
+        v = qkv[:, 2 * d + h * dh:2 * d + (h + 1) * dh]
+        z = np.where(allowed, (q @ k.T) / np.sqrt(dh), -np.inf)
+        for i in np.nonzero(valid)[0]:
+            zi = z[i] - z[i].max()
+            p = np.exp(zi)
+            o[i, h * dh:(h + 1) * dh] = (p / p.sum()) @ v
+    return x + o @ wo.T
+
+
 def rel_err(a, b):
     scale = np.sqrt(np.mean(np.square(b))) if b.size else 1.0
     return float(np.max(np.abs(a - b)) / max(scale, 1e-300)) if b.size else 0.0
@@ -279,6 +306,32 @@ def pin_stages_compose(orc):
     out = orc.out_proj_residual(o, wo, x)
     assert np.array_equal(out, orc.block_mhsa(x, cu, wqkv, wo, 3, 2))
     assert rel_err(qkv, x @ wqkv.T) < 1e-13
+
+
+def pin_padded_buckets(orc):
+    """Padded buckets against a masked brute force written in the padded
+    layout (blocks restart in every bucket, padding is never a key); padding
+    rows return x; what padding rows hold never reaches a valid row; lengths
+    past the bucket are clamped to it."""
+    rng = np.random.default_rng(11)
+    lengths, t, block, heads, d = [7, 0, 12, 3], 12, 5, 2, 16
+    n = len(lengths) * t
+    x = rng.standard_normal((n, d))
+    wqkv = rng.standard_normal((3 * d, d)) / 4
+    wo = rng.standard_normal((d, d)) / 4
+    got = orc.block_mhsa_padded(x, lengths, t, wqkv, wo, block, heads)
+    ref = brute_force_padded(x, lengths, t, wqkv, wo, block, heads)
+    assert rel_err(got, ref) < 1e-12
+    pos = np.arange(n) % t
+    pad = pos >= np.asarray(lengths)[np.arange(n) // t]
+    assert np.array_equal(got[pad], x[pad])
+    x2 = x.copy()
+    x2[pad] = 1e3 * rng.standard_normal((int(pad.sum()), d))
+    got2 = orc.block_mhsa_padded(x2, lengths, t, wqkv, wo, block, heads)
+    assert np.array_equal(got2[~pad], got[~pad])
+    assert np.array_equal(got2[pad], x2[pad])
+    got3 = orc.block_mhsa_padded(x, [7, -4, 99, 3], t, wqkv, wo, block, heads)
+    assert np.array_equal(got3, got)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -109,3 +109,36 @@ def test_stage_argument_errors(lib):
     assert lib.gs_block_attn(FAKE, FAKE, 1, 10, 1024, 8, 200, gsattn.GS_BF16, FAKE, W, 16, None) == gsattn.GS_ERR_WORKSPACE_TOO_SMALL
     assert lib.gs_out_proj_residual(FAKE, FAKE, None, FAKE, 10, 1024, gsattn.GS_F32, None) == gsattn.GS_ERR_INVALID_ARGUMENT
     assert lib.gs_qkv_proj(FAKE, FAKE, FAKE, 1 << 31, 1024, gsattn.GS_BF16, None) == gsattn.GS_ERR_UNSUPPORTED
+
+
+def _fwd_padded(lib, desc, x=FAKE, lengths=FAKE, T=200, wqkv=FAKE, wo=FAKE, B=200, H=8,
+                out=FAKE + (1 << 30)):
+    d = ctypes.byref(desc) if desc is not None else None
+    st = lib.gs_block_mhsa_fwd_padded(x, lengths, T, wqkv, wo, B, H, out, None, d)
+    return st, lib.gs_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("kw,desc_kw,code", [
+    ({}, None, gsattn.GS_ERR_INVALID_ARGUMENT),                       # desc NULL
+    ({"lengths": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"T": 0}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"T": 300}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),                 # S * T != N
+    ({"x": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"out": FAKE + 4096}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),       # partial overlap with x
+    ({"H": 16}, {}, gsattn.GS_ERR_UNSUPPORTED),
+    ({"B": 0}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"S": 0}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"wsb": 1000}, gsattn.GS_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_padded_argument_errors(lib, kw, desc_kw, code):
+    desc = None if desc_kw is None else _desc(**desc_kw)
+    st, detail = _fwd_padded(lib, desc, **kw)
+    assert st == code, (st, detail)
+    assert detail
+
+
+def test_padded_zero_rows_is_rejected(lib):
+    # S >= 1 buckets of T >= 1 rows never hold 0 rows: total_frames = 0 is a mismatch
+    st, detail = _fwd_padded(lib, _desc(S=1, N=0, ws=None, wsb=0), x=None, T=1, wqkv=None,
+                             wo=None, out=None)
+    assert st == gsattn.GS_ERR_INVALID_ARGUMENT and "bucket_frames" in detail

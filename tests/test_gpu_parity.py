@@ -277,6 +277,109 @@ def test_full_sequence_attention_sampled(orc):
         assert torch.equal(one, out[a:b]), f"sequence {s} differs when run alone"
 
 
+# ---------------------------------------------------------------------------
+# padded fixed-length buckets (gs_block_mhsa_fwd_padded)
+
+PADDED = [
+    # lengths, bucket T, B, d, heads
+    ([64, 17, 0], 64, 200, 256, 2),
+    ([300, 129, 5, 300], 300, 128, 256, 2),   # blocks restart inside each bucket
+    ([800, 431, 1, 799], 800, 200, 1024, 8),  # the 800-frame encoder bucket
+    ([0, 0], 40, 16, 128, 1),                 # nothing valid: out = x
+]
+
+
+def _padded_run(lengths, t, block, d, heads, dtype, seed):
+    case = workloads.custom_case([t] * len(lengths), d, heads, block, dtype, seed=seed)
+    wqkv, wo = (w.to(G.dev()) for w in case.weights[0])
+    x = case.x.to(G.dev()).view(len(lengths), t, d)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=G.dev())
+    out = gsattn.block_mhsa_fwd_padded(x, lens, wqkv, wo, block, heads)
+    torch.cuda.synchronize()
+    pos = np.arange(len(lengths) * t) % t
+    valid = pos < np.clip(np.repeat(np.asarray(lengths), t), 0, t)
+    return case, x, lens, wqkv, wo, out, valid
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("lengths,T,B,d,H", PADDED)
+def test_padded_buckets(orc, dtype, lengths, T, B, d, H):
+    """Valid rows against the oracle element by element; padding rows return x
+    exactly; the valid rows are bit for bit those of the packed entry point
+    on the same sequences."""
+    G.print_case("padded", dtype=dtype, lengths=lengths, T=T, B=B, d=d, H=H)
+    case, x, lens, wqkv, wo, out, valid = _padded_run(lengths, T, B, d, H, dtype,
+                                                      seed=sum(lengths) + T)
+    ref = orc.block_mhsa_padded(case.x, lengths, T, case.weights[0][0], case.weights[0][1], B, H)
+    got = out.reshape(-1, d).double().cpu().numpy()
+    err = G.rel_err(got[valid], ref[valid])
+    t = G.tol_for(dtype)
+    print(f"  valid rows={int(valid.sum())} err={err:.3e} tol={t:g}", flush=True)
+    assert err <= t, err
+    flat_x, flat_out = x.reshape(-1, d), out.reshape(-1, d)
+    vt = torch.from_numpy(valid).to(G.dev())
+    assert torch.equal(flat_out[~vt], flat_x[~vt]), "padding rows differ from x"
+    if valid.any():
+        lv = [min(max(l, 0), T) for l in lengths]
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lv)]), dtype=torch.int32, device=G.dev())
+        packed = G.run(flat_x[vt].contiguous(), cu, wqkv, wo, B, H)
+        assert torch.equal(packed, flat_out[vt]), "valid rows differ from the packed entry point"
+
+
+def test_padded_garbage_in_padding_does_not_leak():
+    """Large values in padding rows change neither the valid rows nor their
+    own copy semantics (padding is never a key)."""
+    lengths, t, block, d, heads = [150, 37, 200], 200, 64, 256, 2
+    G.print_case("padded garbage", lengths=lengths, T=t)
+    case, x, lens, wqkv, wo, out, valid = _padded_run(lengths, t, block, d, heads,
+                                                      torch.bfloat16, seed=5)
+    vt = torch.from_numpy(valid).to(G.dev())
+    x2 = x.clone().reshape(-1, d)
+    x2[~vt] = 1000.0
+    out2 = gsattn.block_mhsa_fwd_padded(x2.view_as(x), lens, wqkv, wo, block, heads)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.reshape(-1, d)[vt], out.reshape(-1, d)[vt])
+    assert torch.equal(out2.reshape(-1, d)[~vt], x2[~vt])
+
+
+def test_padded_bucket_workload_sampled(orc):
+    """128 buckets of 800 rows holding the headline batch's lengths capped at
+    800, as the benchmark runs them: sampled buckets against the oracle,
+    padding rows equal to x everywhere, valid rows bit for bit those of the
+    packed entry point on the same sequences."""
+    name = "bf16_bucket800_b128"
+    case = workloads.build_case(workloads.WORKLOADS[name])
+    t, d = case.bucket_frames, case.d_model
+    G.print_case(name, rows=case.x.shape[0], frames=int(case.lengths.sum()))
+    wqkv, wo = (w.to(G.dev()) for w in case.weights[0])
+    x = case.x.to(G.dev()).view(-1, t, d)
+    lens = torch.from_numpy(case.lengths.astype(np.int32)).to(G.dev())
+    out = gsattn.block_mhsa_fwd_padded(x, lens, wqkv, wo, case.block_frames, case.heads)
+    out2 = gsattn.block_mhsa_fwd_padded(x, lens, wqkv, wo, case.block_frames, case.heads)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "run-to-run results differ"
+    s = len(case.lengths)
+    rows = np.arange(s * t)
+    valid = (rows % t) < np.repeat(case.lengths, t)
+    pick = sorted({0, s // 2, s - 1, int(np.argmax(case.lengths)), int(np.argmin(case.lengths))})
+    mask = np.zeros(s * t, np.uint8)
+    for b in pick:
+        mask[b * t:(b + 1) * t] = 1
+    mask &= valid.astype(np.uint8)
+    ref = orc.block_mhsa_padded(case.x, case.lengths, t, case.weights[0][0], case.weights[0][1],
+                                case.block_frames, case.heads, mask=mask)
+    sel = mask.astype(bool)
+    flat = out.reshape(-1, d)
+    err = G.rel_err(flat.double().cpu().numpy()[sel], ref[sel])
+    print(f"  buckets={pick} sampled rows={int(sel.sum())} err={err:.3e}", flush=True)
+    assert err <= G.BF16_TOL, err
+    vt = torch.from_numpy(valid).to(G.dev())
+    assert torch.equal(flat[~vt], x.reshape(-1, d)[~vt]), "padding rows differ from x"
+    cu = torch.from_numpy(case.cu).to(G.dev())
+    packed = G.run(x.reshape(-1, d)[vt].contiguous(), cu, wqkv, wo, case.block_frames, case.heads)
+    assert torch.equal(packed, flat[vt]), "valid rows differ from the packed entry point"
+
+
 def test_workload_chain16_teacher_forced(orc):
     """16 layers with independent weights, each fed the previous layer's GPU output.
 

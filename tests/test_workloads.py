@@ -37,3 +37,11 @@ def test_full_sequence_workload_is_the_long_batch_with_one_block_per_sequence():
     table = accounting.block_table(lengths, full.block_frames)
     assert len(table) == len(lengths)
     assert [l for _, l in table] == [int(v) for v in lengths]
+
+
+def test_bucket_workload_caps_the_headline_lengths():
+    w = workloads.WORKLOADS["bf16_bucket800_b128"]
+    head = workloads.WORKLOADS["bf16_b128_lognormal"].lengths()
+    assert w.bucket_frames == 800
+    assert np.array_equal(w.lengths(), np.minimum(head, 800))
+    assert (head > 800).any()  # the cap matters for some sequences
