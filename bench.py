@@ -98,12 +98,122 @@ def cpu_baseline(case, budget_s: float = 12.0):
                       f"one layer, fp64, {el:.1f} s"}
 
 
+def cpu_baseline_xattn(c, budget_s: float = 12.0):
+    """The window cross-attention oracle, untuned, window by window in order
+    until about `budget_s` seconds have passed."""
+    from oracle import window_xattn as wx
+
+    t0 = time.perf_counter()
+    nw = c.xq.shape[0]
+    row0, lens = wx.window_table(c.cu, c.window_frames)
+    wq, wkv, wo = (t.double().numpy() for t in (c.wq, c.wkv, c.wo))
+    done = frames = 0
+    step = 64
+    while done < nw and time.perf_counter() - t0 < budget_s:
+        ws = range(done, min(nw, done + step))
+        # the windows [done, done + step) cover rows [a, b); a is a window
+        # start, so cutting at a, b and the sequence starts between them
+        # gives the same windows
+        a = int(row0[ws[0]])
+        b = int(row0[ws[-1]] + lens[ws[-1]])
+        cut = sorted({a, b} | {int(v) for v in np.asarray(c.cu, np.int64) if a < v < b})
+        sub_cu = np.asarray([v - a for v in cut], np.int64)
+        wx.window_xattn(c.hcat[a:b].double().numpy(), sub_cu, c.xq[done:done + len(ws)].double().numpy(),
+                        wq, wkv, wo, c.heads, c.window_frames)
+        frames += b - a
+        done += len(ws)
+    el = time.perf_counter() - t0
+    try:  # the oracle's matrix products run on numpy's BLAS threads
+        import threadpoolctl
+        cores = max([p["num_threads"] for p in threadpoolctl.threadpool_info()
+                     if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        cores = None
+    return {"value": frames / el, "unit": "frames/s", "cores": cores,
+            "kind": "oracle", "sample": f"first {done} of {nw} windows ({frames} frames), fp64, "
+                                        f"{el:.1f} s"}
+
+
+def bench_xattn(args):
+    """The window cross-attention of the Q-Former projector on its workload."""
+    w = workloads.XATTN_WORKLOADS[args.workload]
+    c = workloads.build_xattn_case(w)
+    dev = torch.device("cuda:0")
+    hcat, xq = c.hcat.to(dev), c.xq.to(dev)
+    cu = torch.from_numpy(c.cu).to(dev)
+    wq, wkv, wo = c.wq.to(dev), c.wkv.to(dev), c.wo.to(dev)
+    n, f = hcat.shape
+    nw, nq, dq = xq.shape
+    lib = gsattn.load()
+    ws = torch.empty(lib.gs_window_xattn_workspace_bytes(n, dq, nw, nq), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(xq)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None, base=0):
+        gsattn.window_xattn_fwd(hcat, cu, xq, wq, wkv, wo, c.window_frames, c.heads, out=out,
+                                workspace=ws, stream=stream,
+                                kernel_events=events.view(base) if events else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = gsattn.HipEvents(4 * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev, 4 * k)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    names = ("kv_q_proj", "window_attn", "out_proj")
+    avg = {k: float(np.mean([ev.elapsed_ms(4 * i + j, 4 * i + j + 1) for i in range(args.steps)]))
+           for j, k in enumerate(names)}
+    rows = nw * nq
+    fl = {"kv_q_proj": 2.0 * n * f * 2 * dq + 2.0 * rows * dq * dq,
+          "window_attn": 4.0 * nq * n * dq,
+          "out_proj": 2.0 * rows * dq * dq}
+    by = {"kv_q_proj": 2 * (n * f + 2 * dq * f + 2 * n * dq + 2 * rows * dq + dq * dq),
+          "window_attn": 2 * (2 * n * dq + 2 * rows * dq),
+          "out_proj": 2 * (3 * rows * dq + dq * dq)}
+    dom = max(avg, key=avg.get)
+    if by[dom] / (HBM_PEAK_GBS * 1e9) > fl[dom] / (BF16_PEAK_TFLOPS * 1e12):
+        a = by[dom] / (avg[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBS}
+    else:
+        a = fl[dom] / (avg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": a, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": a / BF16_PEAK_TFLOPS}
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    total = sum(fl.values())
+    sec = el / args.steps
+    rec = {
+        "metric": f"encoder frames/sec through the window cross-attention ({w.name}); "
+                  f"% of matrix peak",
+        "value": n / sec, "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": int(len(c.lengths)), "frames": int(n),
+                   "windows": int(nw), "queries": nq, "feat_dim": int(f), "d_q": int(dq),
+                   "heads": c.heads, "window_frames": c.window_frames, "seed": w.seed},
+        "tflops": total / sec / 1e12, "pct_bf16_peak": 100.0 * total / sec / 1e12 / BF16_PEAK_TFLOPS,
+        "useful_gflop": total / 1e9,
+        "kernels": {k: {"avg_ms": avg[k], "tflops": fl[k] / (avg[k] * 1e-3) / 1e12,
+                        "alg_GBs": by[k] / (avg[k] * 1e-3) / 1e9} for k in names},
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_xattn(c, args.cpu_budget),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=workloads.HEADLINE, choices=workloads.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default=workloads.HEADLINE,
+                    choices=workloads.WORKLOAD_ORDER + list(workloads.XATTN_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -131,6 +241,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
         return
 
+    if args.workload in workloads.XATTN_WORKLOADS:
+        bench_xattn(args)
+        return
     w = workloads.WORKLOADS[args.workload]
     case = workloads.build_case(w, layers=w.layers)
     dev = torch.device("cuda:0")

@@ -473,4 +473,14 @@ hipError_t launch_out_proj_bf16_pp(const void* o, const void* wo, const void* x,
                          stream);
 }
 
+// C[M][Nc] = A[M][K] . W[Nc][K]^T (+ R[M][Nc] when R is not null), for any
+// Nc % 256 == 0 and K % 64 == 0 (the window cross-attention's projections).
+hipError_t launch_gemm_nt_bf16_pp(const void* A, const void* W, const void* R, void* C, int M,
+                                  int Nc, int K, hipStream_t stream) {
+  if (R)
+    return pp_launch<true>((const bf16*)A, (const bf16*)W, (const bf16*)R, (bf16*)C, M, Nc, K,
+                           stream);
+  return pp_launch<false>((const bf16*)A, (const bf16*)W, nullptr, (bf16*)C, M, Nc, K, stream);
+}
+
 }  // namespace gs

@@ -23,6 +23,11 @@ hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long
                                   int heads, int B, void* o, void* table, hipStream_t stream);
 hipError_t launch_qkv_proj_f32(const void* x, const void* wqkv, void* qkv, int M, int d,
                                hipStream_t stream);
+hipError_t launch_gemm_nt_bf16_pp(const void* A, const void* W, const void* R, void* C, int M,
+                                  int Nc, int K, hipStream_t stream);
+hipError_t launch_window_attn_bf16(const void* kv, const void* q, const int* cu, int S, int W,
+                                   int nq, int heads, int dq, int window, void* table,
+                                   void* o, hipStream_t stream);
 hipError_t launch_out_proj_f32(const void* o, const void* wo, const void* x, void* out, int M,
                                int d, hipStream_t stream);
 hipError_t launch_block_attn_f32(const void* qkv, SeqSpans sp, int S, long long N, int d,
@@ -373,6 +378,105 @@ gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_
   GS_TRY(record(desc, 2, stream));
   GS_TRY(gs_out_proj_residual(p.o, Wo, x, out, p.N, p.d, desc->dtype, stream));
   GS_TRY(record(desc, 3, stream));
+  return GS_OK;
+}
+
+size_t gs_window_xattn_workspace_bytes(int64_t total_frames, int32_t d_q, int32_t num_windows,
+                                       int32_t queries) {
+  if (total_frames < 0 || d_q < 1 || num_windows < 0 || queries < 1) return 0;
+  const size_t n = (size_t)total_frames, dq = (size_t)d_q;
+  const size_t rows = (size_t)num_windows * queries;
+  // K|V, Q, O, the window table (8 bytes per window and a count), a debug slot
+  return align_up(n * 2 * dq * 2) + 2 * align_up(rows * dq * 2) +
+         align_up(8 * (size_t)num_windows + 4) + kAlign;
+}
+
+gs_status gs_window_xattn_fwd(const void* hcat, const int32_t* cu_seqlens, const void* xq,
+                              const void* Wq, const void* Wkv, const void* Wo,
+                              int32_t window_frames, int32_t heads, void* out,
+                              hipStream_t stream, const gs_xattn_desc* desc) {
+  if (!desc) return fail(GS_ERR_INVALID_ARGUMENT, "desc is NULL");
+  GS_TRY(check_dtype(desc->dtype));
+  if (desc->dtype != GS_BF16)
+    return fail(GS_ERR_UNSUPPORTED, "window cross-attention is implemented for bf16 only");
+  const int64_t N = desc->total_frames;
+  const int32_t F = desc->feat_dim, dq = desc->d_q, W = desc->num_windows, nq = desc->queries;
+  if (desc->num_seqs < 1) return fail(GS_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", desc->num_seqs);
+  if (N < 0) return fail(GS_ERR_INVALID_ARGUMENT, "total_frames %lld < 0", (long long)N);
+  if (W < 0) return fail(GS_ERR_INVALID_ARGUMENT, "num_windows %d < 0", W);
+  if (nq < 1 || nq > 4) return fail(GS_ERR_UNSUPPORTED, "queries %d: 1 to 4 are implemented", nq);
+  if (window_frames < 1) return fail(GS_ERR_INVALID_ARGUMENT, "window_frames %d < 1", window_frames);
+  if (F < 1 || dq < 1) return fail(GS_ERR_INVALID_ARGUMENT, "feat_dim %d or d_q %d < 1", F, dq);
+  if (heads < 1 || dq % heads != 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "d_q %d is not a multiple of heads %d", dq, heads);
+  if (dq / heads != kDh) return fail(GS_ERR_UNSUPPORTED, "head dim %d: dh = 128 is implemented", dq / heads);
+  if (dq % 256 != 0 || dq > kMaxD || F % 64 != 0 || F > 4 * kMaxD)
+    return fail(GS_ERR_UNSUPPORTED, "d_q %d (multiple of 256, at most %d) or feat_dim %d "
+                "(multiple of 64, at most %d)", dq, kMaxD, F, 4 * kMaxD);
+  if (N >= (int64_t)1 << 31 || (int64_t)W * nq >= (int64_t)1 << 31 ||
+      (__int128)N * 2 * dq >= ((__int128)1 << 62))
+    return fail(GS_ERR_UNSUPPORTED, "sizes exceed the 32-bit row counts of the kernels");
+  if (!cu_seqlens) return fail(GS_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  if (W == 0) return GS_OK;
+  GS_TRY(check_ptr(xq, "xq"));
+  GS_TRY(check_ptr(Wq, "Wq"));
+  GS_TRY(check_ptr(Wkv, "Wkv"));
+  GS_TRY(check_ptr(Wo, "Wo"));
+  GS_TRY(check_ptr(out, "out"));
+  if (N > 0) GS_TRY(check_ptr(hcat, "hcat"));
+  const size_t rows = (size_t)W * nq;
+  const size_t qbytes = rows * dq * 2;
+  if (out != xq) {
+    const char* a = (const char*)xq;
+    const char* b = (const char*)out;
+    if (a < b + qbytes && b < a + qbytes)
+      return fail(GS_ERR_INVALID_ARGUMENT, "out partially overlaps xq");
+  }
+  const size_t need = gs_window_xattn_workspace_bytes(N, dq, W, nq);
+  if (!desc->workspace) return fail(GS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (((uintptr_t)desc->workspace & (kAlign - 1)) != 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (desc->workspace_bytes < need)
+    return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                desc->workspace_bytes, need);
+  char* ws = (char*)desc->workspace;
+  void* kv = ws;
+  void* q = ws + align_up((size_t)N * 2 * dq * 2);
+  void* o = (char*)q + align_up(qbytes);
+  char* table = (char*)o + align_up(qbytes);
+  int* dflag = (int*)(table + align_up(8 * (size_t)W + 4));
+  if (debug_checks()) {
+    if (N > 0) GS_TRY(debug_check_cu(cu_seqlens, desc->num_seqs, N, dflag, stream));
+    // the window count the sequences make
+    GS_TRY(hip_status(gs::launch_window_attn_bf16(kv, q, cu_seqlens, desc->num_seqs, 0, nq, heads,
+                                                  dq, window_frames, table, o, stream),
+                      "window table launch"));
+    int count = -1;
+    GS_TRY(hip_status(hipMemcpyAsync(&count, table, sizeof(int), hipMemcpyDeviceToHost, stream),
+                      "window count copy"));
+    GS_TRY(hip_status(hipStreamSynchronize(stream), "window count sync"));
+    if (count != W)
+      return fail(GS_ERR_INVALID_ARGUMENT, "num_windows %d, the sequences make %d", W, count);
+  }
+
+  auto rec = [&](int i) -> gs_status {
+    if (!desc->kernel_events) return GS_OK;
+    return hip_status(hipEventRecord(desc->kernel_events[i], stream), "hipEventRecord");
+  };
+  GS_TRY(rec(0));
+  if (N > 0)
+    GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp(hcat, Wkv, nullptr, kv, (int)N, 2 * dq, F, stream),
+                      "K|V projection launch"));
+  GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp(xq, Wq, nullptr, q, (int)rows, dq, dq, stream),
+                    "Q projection launch"));
+  GS_TRY(rec(1));
+  GS_TRY(hip_status(gs::launch_window_attn_bf16(kv, q, cu_seqlens, desc->num_seqs, W, nq, heads,
+                                                dq, window_frames, table, o, stream),
+                    "window attention launch"));
+  GS_TRY(rec(2));
+  GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp(o, Wo, xq, out, (int)rows, dq, dq, stream),
+                    "output projection launch"));
+  GS_TRY(rec(3));
   return GS_OK;
 }
 

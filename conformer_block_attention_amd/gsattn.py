@@ -23,7 +23,8 @@ EXPORTS = (
     "gs_block_mhsa_workspace_bytes", "gs_block_mhsa_fwd", "gs_block_mhsa_fwd_padded",
     "gs_qkv_proj", "gs_block_attn",
     "gs_block_attn_workspace_bytes", "gs_out_proj_residual", "gs_status_string",
-    "gs_last_error_detail", "gs_version",
+    "gs_last_error_detail", "gs_version", "gs_window_xattn_workspace_bytes",
+    "gs_window_xattn_fwd",
 )
 
 
@@ -40,6 +41,21 @@ class _Desc(ctypes.Structure):
         ("num_seqs", ctypes.c_int32),
         ("total_frames", ctypes.c_int64),
         ("d_model", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("kernel_events", ctypes.c_void_p),
+    ]
+
+
+class _XattnDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_frames", ctypes.c_int64),
+        ("feat_dim", ctypes.c_int32),
+        ("d_q", ctypes.c_int32),
+        ("num_windows", ctypes.c_int32),
+        ("queries", ctypes.c_int32),
         ("dtype", ctypes.c_int),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
@@ -67,6 +83,11 @@ def load(path: Optional[str] = None):
     lib.gs_block_mhsa_fwd_padded.restype = ctypes.c_int
     lib.gs_block_mhsa_fwd_padded.argtypes = [P, P, I32, P, P, I32, I32, P, P,
                                              ctypes.POINTER(_Desc)]
+    lib.gs_window_xattn_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_window_xattn_workspace_bytes.argtypes = [I64, I32, I32, I32]
+    lib.gs_window_xattn_fwd.restype = ctypes.c_int
+    lib.gs_window_xattn_fwd.argtypes = [P, P, P, P, P, P, I32, I32, P, P,
+                                        ctypes.POINTER(_XattnDesc)]
     lib.gs_qkv_proj.restype = ctypes.c_int
     lib.gs_qkv_proj.argtypes = [P, P, P, I64, I32, ctypes.c_int, P]
     lib.gs_block_attn.restype = ctypes.c_int
@@ -173,6 +194,34 @@ def block_mhsa_fwd_padded(x: torch.Tensor, lengths: torch.Tensor, wqkv: torch.Te
         _dev(x, "x"), _dev(lengths, "lengths"), int(t), _dev(wqkv, "Wqkv", x.dtype),
         _dev(wo, "Wo", x.dtype), int(block_frames), int(heads), _dev(out, "out", x.dtype),
         _stream(stream), ctypes.byref(desc)))
+    return out
+
+
+def window_xattn_fwd(hcat: torch.Tensor, cu_seqlens: torch.Tensor, xq: torch.Tensor,
+                     wq: torch.Tensor, wkv: torch.Tensor, wo: torch.Tensor, window_frames: int,
+                     heads: int, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None,
+                     kernel_events: Optional["HipEvents"] = None) -> torch.Tensor:
+    """Window cross-attention: hcat [N, F], xq [W, nq, dq] -> out [W, nq, dq]."""
+    lib = load()
+    n, f = hcat.shape
+    nw, nq, dq = xq.shape
+    dt = _gs_dtype(xq.dtype)
+    if out is None:
+        out = torch.empty_like(xq)
+    if workspace is None:
+        nb = lib.gs_window_xattn_workspace_bytes(n, dq, nw, nq)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=xq.device)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    desc = _XattnDesc(int(cu_seqlens.numel()) - 1, int(n), int(f), int(dq), int(nw), int(nq), dt,
+                      workspace.data_ptr(), int(workspace.numel()),
+                      kernel_events.handle_array() if kernel_events else None)
+    _check(lib.gs_window_xattn_fwd(
+        _dev(hcat, "hcat", xq.dtype), _dev(cu_seqlens, "cu_seqlens"), _dev(xq, "xq"),
+        _dev(wq, "Wq", xq.dtype), _dev(wkv, "Wkv", xq.dtype), _dev(wo, "Wo", xq.dtype),
+        int(window_frames), int(heads), _dev(out, "out", xq.dtype), _stream(stream),
+        ctypes.byref(desc)))
     return out
 
 

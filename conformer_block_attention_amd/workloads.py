@@ -199,3 +199,61 @@ def custom_case(lengths, d_model: int, heads: int, block_frames: int, dtype: tor
     x = make_x(n, d_model, dtype, seed)
     weights = [make_weights(d_model, dtype, seed, l) for l in range(layers)]
     return Case(name, lengths, cu, x, weights, block_frames, heads, dtype)
+
+
+# The window cross-attention of the Q-Former projector (IBM model card, "Model
+# Architecture" (2)): 15-frame windows of the concatenated states of four
+# encoder layers (F = 4 x 1024) reduced to 3 queries each.  The pages give no
+# widths: dq = 2048 with 16 heads of 128 is the width at which two layers of
+# self-attention, cross-attention (K|V from F = 4096) and a 4x feed-forward
+# come to the stated 160 M parameters (about 75 M per layer).  Frames: the
+# headline batch's lengths.  Random streams: 1 hcat, 2 Wq, 3 Wkv, 4 Wo, 5 xq;
+# weights N(0, 1/fan_in), hcat and xq N(0, 1).
+@dataclasses.dataclass(frozen=True)
+class XattnWorkload:
+    name: str
+    lengths_from: str = "bf16_b128_lognormal"
+    feat_dim: int = 4096
+    d_q: int = 2048
+    heads: int = 16
+    window_frames: int = 15
+    queries: int = 3
+    seed: int = 0
+
+
+@dataclasses.dataclass
+class XattnCase:
+    name: str
+    lengths: np.ndarray
+    cu: np.ndarray
+    hcat: torch.Tensor        # [N, F] bf16
+    xq: torch.Tensor          # [W, nq, dq] bf16
+    wq: torch.Tensor          # [dq, dq]
+    wkv: torch.Tensor         # [2 dq, F]
+    wo: torch.Tensor          # [dq, dq]
+    window_frames: int
+    heads: int
+
+
+def num_windows(lengths, window: int) -> int:
+    lengths = np.asarray(lengths, np.int64)
+    return int(np.sum((lengths + window - 1) // window))
+
+
+def build_xattn_case(w: XattnWorkload, lengths=None) -> XattnCase:
+    if lengths is None:
+        lengths = WORKLOADS[w.lengths_from].lengths()
+    lengths = np.asarray(lengths, np.int64)
+    cu = cu_seqlens(lengths)
+    n = int(cu[-1])
+    nw = num_windows(lengths, w.window_frames)
+    f, dq, bf = w.feat_dim, w.d_q, torch.bfloat16
+    hcat = normal(w.seed, 1, (n, f)).to(bf)
+    wq = normal(w.seed, 2, (dq, dq), 1.0 / math.sqrt(dq)).to(bf)
+    wkv = normal(w.seed, 3, (2 * dq, f), 1.0 / math.sqrt(f)).to(bf)
+    wo = normal(w.seed, 4, (dq, dq), 1.0 / math.sqrt(dq)).to(bf)
+    xq = normal(w.seed, 5, (nw, w.queries, dq)).to(bf)
+    return XattnCase(w.name, lengths, cu, hcat, xq, wq, wkv, wo, w.window_frames, w.heads)
+
+
+XATTN_WORKLOADS = {"bf16_qformer_xattn_b128": XattnWorkload("bf16_qformer_xattn_b128")}

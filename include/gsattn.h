@@ -158,6 +158,55 @@ gs_status gs_out_proj_residual(const void* o, const void* Wo, const void* x, voi
                                int64_t total_frames, int32_t d_model, gs_dtype dtype,
                                hipStream_t stream);
 
+/*
+ * Window cross-attention of the Q-Former projector (IBM model card, "Model
+ * Architecture" (2) Q-Former Projector: each 15-frame window of the
+ * concatenated states of encoder layers 4, 8, 12, 16 is reduced to 3 queries
+ * by cross-attention).  The pages give no widths, head count or bias terms;
+ * this entry point computes, for every window w of every sequence (runs of
+ * window_frames rows from the sequence's first row, the last one holding the
+ * remainder) and each of its nq query rows i:
+ *   q = xq[w][i] . Wq^T;  k_l | v_l = hcat[l] . Wkv^T for the window's rows l
+ *   o = per head (dh = 128): softmax_l(q . k_l / sqrt(dh)) v_l
+ *   out[w][i] = xq[w][i] + o . Wo^T
+ * bf16 storage, fp32 accumulation, every fp32->bf16 conversion rounds to
+ * nearest even.  Device pointers, caller-owned, 16-byte aligned:
+ *   hcat  [N][F]          frames (F = feat_dim, e.g. 4 x 1024 for four layers)
+ *   cu_seqlens [S+1]      int32 sequence offsets into hcat (as gs_block_mhsa_fwd)
+ *   xq    [W][nq][dq]     query states per window
+ *   Wq    [dq][dq], Wkv [2 dq][F] (K rows then V rows), Wo [dq][dq]
+ *   out   [W][nq][dq]     may equal xq; any other overlap is invalid
+ * W = num_windows must equal sum_s ceil(len_s / window_frames) (checked on
+ * the device, with a synchronisation, only under GSATTN_DEBUG_CHECKS=1;
+ * otherwise windows past the sequences' count get o = 0).  Supported: bf16,
+ * dq % 256 == 0 with dq / heads == 128, F % 64 == 0, 1 <= nq <= 4,
+ * window_frames >= 1.  Kernel events (if given): before the projections of
+ * K|V and Q, after them, after the attention step, after the output
+ * projection.
+ */
+typedef struct {
+  int32_t num_seqs;        /* S >= 1 */
+  int64_t total_frames;    /* N = cu_seqlens[S] */
+  int32_t feat_dim;        /* F */
+  int32_t d_q;             /* dq */
+  int32_t num_windows;     /* W */
+  int32_t queries;         /* nq */
+  gs_dtype dtype;          /* GS_BF16 */
+  void* workspace;         /* >= gs_window_xattn_workspace_bytes() bytes, 256-byte aligned */
+  size_t workspace_bytes;
+  hipEvent_t* kernel_events;  /* NULL or four events */
+} gs_xattn_desc;
+
+/* Bytes of workspace gs_window_xattn_fwd needs (0 on bad input): K|V
+   [N][2 dq], Q and O [W*nq][dq], the window table. */
+size_t gs_window_xattn_workspace_bytes(int64_t total_frames, int32_t d_q, int32_t num_windows,
+                                       int32_t queries);
+
+gs_status gs_window_xattn_fwd(const void* hcat, const int32_t* cu_seqlens, const void* xq,
+                              const void* Wq, const void* Wkv, const void* Wo,
+                              int32_t window_frames, int32_t heads, void* out,
+                              hipStream_t stream, const gs_xattn_desc* desc);
+
 /* Static text for a status code. */
 const char* gs_status_string(gs_status s);
 

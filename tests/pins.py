@@ -334,4 +334,76 @@ def pin_padded_buckets(orc):
     assert np.array_equal(got3, got)
 
 
+def _xattn_problem(lengths, window, nq=3, f=24, dq=16, seed=0):
+    rng = np.random.default_rng(seed)
+    cu = np.zeros(len(lengths) + 1, np.int64)
+    cu[1:] = np.cumsum(lengths)
+    from oracle import window_xattn as wx
+    nw = wx.num_windows(cu, window)
+    hcat = rng.standard_normal((int(cu[-1]), f))
+    xq = rng.standard_normal((nw, nq, dq))
+    wq = rng.standard_normal((dq, dq)) / 4
+    wkv = rng.standard_normal((2 * dq, f)) / 5
+    wo = rng.standard_normal((dq, dq)) / 4
+    return cu, hcat, xq, wq, wkv, wo
+
+
+def pin_window_xattn_brute_force(orc):
+    """Window cross-attention against one masked attention over all frames:
+    every query row of every window against every frame, with a mask that
+    keeps only the frames of its own window."""
+    from oracle import window_xattn as wx
+    lengths, window, heads = [31, 15, 4, 0, 16], 15, 2
+    cu, hcat, xq, wq, wkv, wo = _xattn_problem(lengths, window, seed=3)
+    got = wx.window_xattn(hcat, cu, xq, wq, wkv, wo, heads, window)
+    nw, nq, dq = xq.shape
+    dh = dq // heads
+    # window index of every frame, by walking the sequences frame by frame
+    win_of = np.full(int(cu[-1]), -1)
+    w = 0
+    for s in range(len(lengths)):
+        for j in range(lengths[s]):
+            win_of[cu[s] + j] = w + j // window
+        w += -(-lengths[s] // window)
+    assert w == nw and (win_of >= 0).all()
+    q = xq.reshape(nw * nq, dq) @ wq.T
+    k = hcat @ wkv[:dq].T
+    v = hcat @ wkv[dq:].T
+    qwin = np.repeat(np.arange(nw), nq)
+    allowed = qwin[:, None] == win_of[None, :]
+    o = np.zeros((nw * nq, dq))
+    for h in range(heads):
+        c = slice(h * dh, (h + 1) * dh)
+        z = np.where(allowed, (q[:, c] @ k[:, c].T) / np.sqrt(dh), -np.inf)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        o[:, c] = (p / p.sum(axis=1, keepdims=True)) @ v[:, c]
+    ref = (xq.reshape(nw * nq, dq) + o @ wo.T).reshape(nw, nq, dq)
+    assert rel_err(got, ref) < 1e-12
+
+
+def pin_window_xattn_closed_forms(orc):
+    """A one-frame window gives every query that frame's value row (softmax
+    weight 1): out = xq + (h Wv^T) Wo^T; Wo = 0 gives out = xq; frames
+    permuted inside a window change nothing; the windows of a sequence do
+    not see each other (changing one window's frames leaves the others)."""
+    from oracle import window_xattn as wx
+    cu, hcat, xq, wq, wkv, wo = _xattn_problem([1, 1, 3], 1, seed=4)
+    dq = xq.shape[2]
+    got = wx.window_xattn(hcat, cu, xq, wq, wkv, wo, 2, 1)
+    ref = xq + ((hcat @ wkv[dq:].T) @ wo.T)[:, None, :]
+    assert rel_err(got, ref) < 1e-13
+    cu, hcat, xq, wq, wkv, wo = _xattn_problem([40, 7], 15, seed=5)
+    z = wx.window_xattn(hcat, cu, xq, wq, wkv, np.zeros_like(wo), 2, 15)
+    assert np.array_equal(z, xq)
+    base = wx.window_xattn(hcat, cu, xq, wq, wkv, wo, 2, 15)
+    perm = hcat.copy()
+    perm[15:30] = perm[15:30][::-1]
+    assert rel_err(wx.window_xattn(perm, cu, xq, wq, wkv, wo, 2, 15), base) < 1e-13
+    other = hcat.copy()
+    other[15:30] += 3.0
+    moved = wx.window_xattn(other, cu, xq, wq, wkv, wo, 2, 15)
+    assert np.array_equal(moved[[0, 2, 3]], base[[0, 2, 3]])
+    assert not np.allclose(moved[1], base[1])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -142,3 +142,54 @@ def test_padded_zero_rows_is_rejected(lib):
     st, detail = _fwd_padded(lib, _desc(S=1, N=0, ws=None, wsb=0), x=None, T=1, wqkv=None,
                              wo=None, out=None)
     assert st == gsattn.GS_ERR_INVALID_ARGUMENT and "bucket_frames" in detail
+
+
+def _xdesc(S=2, N=400, F=4096, dq=2048, W=30, nq=3, dt=gsattn.GS_BF16, ws=FAKE, wsb=1 << 40):
+    return gsattn._XattnDesc(S, N, F, dq, W, nq, dt, ws, wsb, None)
+
+
+def _xfwd(lib, desc, hcat=FAKE, cu=FAKE, xq=FAKE, wq=FAKE, wkv=FAKE, wo=FAKE, win=15, H=16,
+          out=FAKE + (1 << 30)):
+    d = ctypes.byref(desc) if desc is not None else None
+    st = lib.gs_window_xattn_fwd(hcat, cu, xq, wq, wkv, wo, win, H, out, None, d)
+    return st, lib.gs_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("kw,desc_kw,code", [
+    ({}, None, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"dt": gsattn.GS_F32}, gsattn.GS_ERR_UNSUPPORTED),
+    ({"cu": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"xq": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"wkv": FAKE + 8}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"hcat": None}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"win": 0}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({"H": 3}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),            # 2048 % 3
+    ({"H": 32}, {}, gsattn.GS_ERR_UNSUPPORTED),                # dh = 64
+    ({}, {"nq": 5}, gsattn.GS_ERR_UNSUPPORTED),
+    ({}, {"dq": 128 * 3, "S": 2}, gsattn.GS_ERR_UNSUPPORTED),  # dq % 256
+    ({"H": 3}, {"dq": 384}, gsattn.GS_ERR_UNSUPPORTED),
+    ({}, {"F": 100}, gsattn.GS_ERR_UNSUPPORTED),
+    ({}, {"W": -1}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"S": 0}, gsattn.GS_ERR_INVALID_ARGUMENT),
+    ({}, {"wsb": 4096}, gsattn.GS_ERR_WORKSPACE_TOO_SMALL),
+    ({"out": FAKE + 4096}, {}, gsattn.GS_ERR_INVALID_ARGUMENT),  # partial overlap with xq
+])
+def test_window_xattn_argument_errors(lib, kw, desc_kw, code):
+    desc = None if desc_kw is None else _xdesc(**desc_kw)
+    st, detail = _xfwd(lib, desc, **kw)
+    assert st == code, (st, detail)
+    assert detail
+
+
+def test_window_xattn_no_windows_is_noop(lib):
+    st, _ = _xfwd(lib, _xdesc(N=0, W=0, ws=None, wsb=0), hcat=None, xq=None, wq=None, wkv=None,
+                  wo=None, out=None)
+    assert st == gsattn.GS_OK
+
+
+def test_window_xattn_workspace_bytes(lib):
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    n, dq, w, nq = 1000, 2048, 70, 3
+    assert lib.gs_window_xattn_workspace_bytes(n, dq, w, nq) == (
+        al(n * 2 * dq * 2) + 2 * al(w * nq * dq * 2) + al(8 * w + 4) + 256)
+    assert lib.gs_window_xattn_workspace_bytes(-1, dq, w, nq) == 0
