@@ -207,13 +207,87 @@ def bench_xattn(args):
     print(json.dumps(rec), flush=True)
 
 
+CTC_WORKLOAD = "bpe_pool_ctc_b128"
+
+
+def bench_ctc(args):
+    """Posterior-weighted pooling + CTC greedy decoding of the BPE head's
+    logits for the headline batch's frames (HBM-bound: the logits are read
+    once)."""
+    lengths = workloads.WORKLOADS[workloads.HEADLINE].lengths()
+    logits, bp, cu = workloads.bpe_inputs(lengths)
+    n, ld = logits.shape
+    classes = workloads.BPE_CLASSES
+    lib = gsattn.load()
+    npos = int(np.sum((lengths + 1) // 2))
+    dev = logits.device
+    out = (torch.empty(npos, dtype=torch.int32, device=dev),
+           torch.empty(npos, dtype=torch.int32, device=dev),
+           torch.empty(len(lengths), dtype=torch.int32, device=dev))
+    ws = torch.empty(lib.gs_bpe_ctc_workspace_bytes(len(lengths), npos), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        gsattn.bpe_pool_ctc_greedy(logits, bp, cu, classes, num_positions=npos, workspace=ws,
+                                   out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    by = 2 * n * ld + 4 * n + 8 * npos + 4 * len(lengths)  # logits, blank probs, outputs
+    gbs = by / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ctc_pool as cp
+        t1 = time.perf_counter()
+        cuh = workloads.cu_seqlens(lengths)
+        frames = seqs = 0
+        while seqs < len(lengths) and time.perf_counter() - t1 < args.cpu_budget:
+            a, b = int(cuh[seqs]), int(cuh[seqs + 1])
+            ids = cp.pooled_argmax(logits[a:b, :classes].float().cpu().numpy(),
+                                   bp[a:b].cpu().numpy(), [0, b - a])
+            cp.ctc_greedy(ids, [len(ids)])
+            frames += b - a
+            seqs += 1
+        ce = time.perf_counter() - t1
+        cpu = {"value": frames / ce, "unit": "frames/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {seqs} of {len(lengths)} sequences ({frames} frames), "
+                         f"{ce:.1f} s (includes copying their logits to the host)"}
+    rec = {
+        "metric": f"encoder frames/sec through BPE pooling + CTC greedy decoding ({CTC_WORKLOAD}); "
+                  f"% of HBM peak",
+        "value": n / (ms * 1e-3), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "wall_ms_per_step": el / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CTC_WORKLOAD, "global_batch": int(len(lengths)), "frames": int(n),
+                   "positions": npos, "classes": classes, "ld": int(ld), "window": 4,
+                   "stride": 2},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "kernel": "pooled_argmax + collapse",
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=workloads.HEADLINE,
-                    choices=workloads.WORKLOAD_ORDER + list(workloads.XATTN_WORKLOADS))
+                    choices=workloads.WORKLOAD_ORDER + list(workloads.XATTN_WORKLOADS) +
+                    [CTC_WORKLOAD])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -243,6 +317,9 @@ def main():
 
     if args.workload in workloads.XATTN_WORKLOADS:
         bench_xattn(args)
+        return
+    if args.workload == CTC_WORKLOAD:
+        bench_ctc(args)
         return
     w = workloads.WORKLOADS[args.workload]
     case = workloads.build_case(w, layers=w.layers)

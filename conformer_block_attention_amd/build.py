@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgsattn.so")
 
 SOURCES = ["gsattn_api.hip", "gemm_bf16.hip", "gemm_pp_bf16.hip", "gemm_f32.hip", "attn_bf16.hip",
-           "attn_f32.hip", "window_xattn.hip"]
+           "attn_f32.hip", "window_xattn.hip", "ctc_pool.hip"]
 
 # Per-source code-generation options (none at present).
 # The attention kernel never produces NaN from finite inputs; without NaN

@@ -23,6 +23,10 @@ hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long
                                   int heads, int B, void* o, void* table, hipStream_t stream);
 hipError_t launch_qkv_proj_f32(const void* x, const void* wqkv, void* qkv, int M, int d,
                                hipStream_t stream);
+hipError_t launch_bpe_pool_ctc(const void* logits, long long ld, const float* blank_prob,
+                               const int* cu, int S, int C, int P, int window, int stride,
+                               int* argmax, int* tokens, int* counts, void* workspace,
+                               hipStream_t stream);
 hipError_t launch_gemm_nt_bf16_pp(const void* A, const void* W, const void* R, void* C, int M,
                                   int Nc, int K, hipStream_t stream);
 hipError_t launch_window_attn_bf16(const void* kv, const void* q, const int* cu, int S, int W,
@@ -478,6 +482,49 @@ gs_status gs_window_xattn_fwd(const void* hcat, const int32_t* cu_seqlens, const
                     "output projection launch"));
   GS_TRY(rec(3));
   return GS_OK;
+}
+
+size_t gs_bpe_ctc_workspace_bytes(int32_t num_seqs, int32_t num_positions) {
+  if (num_seqs < 1 || num_positions < 0) return 0;
+  // position table (16 bytes per position, at least one), first positions [S+1]
+  return align_up(16 * ((size_t)(num_positions > 0 ? num_positions : 1)) +
+                  4 * ((size_t)num_seqs + 1));
+}
+
+gs_status gs_bpe_pool_ctc_greedy(const void* logits, int64_t ld, const float* blank_prob,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int64_t total_frames, int32_t num_classes, int32_t window,
+                                 int32_t stride, int32_t num_positions, int32_t* argmax,
+                                 int32_t* tokens, int32_t* token_counts, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 1) return fail(GS_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", num_seqs);
+  if (total_frames < 0) return fail(GS_ERR_INVALID_ARGUMENT, "total_frames < 0");
+  if (total_frames >= (int64_t)1 << 31) return fail(GS_ERR_UNSUPPORTED, "total_frames >= 2^31");
+  if (num_classes < 1) return fail(GS_ERR_INVALID_ARGUMENT, "num_classes %d < 1", num_classes);
+  if (ld < num_classes || ld % 8 != 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "ld %lld: at least num_classes and a multiple of 8",
+                (long long)ld);
+  if (window < 1 || window > 8) return fail(GS_ERR_UNSUPPORTED, "window %d: 1 to 8", window);
+  if (stride < 1) return fail(GS_ERR_INVALID_ARGUMENT, "stride %d < 1", stride);
+  if (num_positions < 0) return fail(GS_ERR_INVALID_ARGUMENT, "num_positions < 0");
+  if (!cu_seqlens || !token_counts)
+    return fail(GS_ERR_INVALID_ARGUMENT, "cu_seqlens or token_counts is NULL");
+  if (num_positions > 0) {
+    if (!argmax || !tokens) return fail(GS_ERR_INVALID_ARGUMENT, "argmax or tokens is NULL");
+    GS_TRY(check_ptr(logits, "logits"));
+    if (!blank_prob) return fail(GS_ERR_INVALID_ARGUMENT, "blank_prob is NULL");
+  }
+  if (!workspace) return fail(GS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  const size_t need = gs_bpe_ctc_workspace_bytes(num_seqs, num_positions);
+  if (workspace_bytes < need)
+    return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes,
+                need);
+  return hip_status(gs::launch_bpe_pool_ctc(logits, ld, blank_prob, cu_seqlens, num_seqs,
+                                            num_classes, num_positions, window, stride, argmax,
+                                            tokens, token_counts, workspace, stream),
+                    "pooling / decoding launch");
 }
 
 }  // extern "C"

@@ -24,7 +24,7 @@ EXPORTS = (
     "gs_qkv_proj", "gs_block_attn",
     "gs_block_attn_workspace_bytes", "gs_out_proj_residual", "gs_status_string",
     "gs_last_error_detail", "gs_version", "gs_window_xattn_workspace_bytes",
-    "gs_window_xattn_fwd",
+    "gs_window_xattn_fwd", "gs_bpe_ctc_workspace_bytes", "gs_bpe_pool_ctc_greedy",
 )
 
 
@@ -88,6 +88,11 @@ def load(path: Optional[str] = None):
     lib.gs_window_xattn_fwd.restype = ctypes.c_int
     lib.gs_window_xattn_fwd.argtypes = [P, P, P, P, P, P, I32, I32, P, P,
                                         ctypes.POINTER(_XattnDesc)]
+    lib.gs_bpe_ctc_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_bpe_ctc_workspace_bytes.argtypes = [I32, I32]
+    lib.gs_bpe_pool_ctc_greedy.restype = ctypes.c_int
+    lib.gs_bpe_pool_ctc_greedy.argtypes = [P, I64, P, P, I32, I64, I32, I32, I32, I32, P, P, P, P,
+                                           ctypes.c_size_t, P]
     lib.gs_qkv_proj.restype = ctypes.c_int
     lib.gs_qkv_proj.argtypes = [P, P, P, I64, I32, ctypes.c_int, P]
     lib.gs_block_attn.restype = ctypes.c_int
@@ -223,6 +228,41 @@ def window_xattn_fwd(hcat: torch.Tensor, cu_seqlens: torch.Tensor, xq: torch.Ten
         int(window_frames), int(heads), _dev(out, "out", xq.dtype), _stream(stream),
         ctypes.byref(desc)))
     return out
+
+
+def bpe_pool_ctc_greedy(logits: torch.Tensor, blank_prob: torch.Tensor, cu_seqlens: torch.Tensor,
+                        num_classes: int, window: int = 4, stride: int = 2,
+                        num_positions: Optional[int] = None, workspace=None, stream=None,
+                        out=None):
+    """Pooled argmax and CTC greedy tokens.  logits [N, ld] bf16 (the first
+    num_classes columns are the classes), blank_prob [N] fp32.  Returns
+    (argmax [P], tokens [P], token_counts [S]) int32 device tensors; sequence
+    s's tokens start at its first position (the prefix sum of the position
+    counts)."""
+    lib = load()
+    n, ld = logits.shape
+    s = int(cu_seqlens.numel()) - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if num_positions is None:  # (reads cu_seqlens on the host)
+        ln = torch.diff(cu_seqlens.cpu().long())
+        num_positions = int(((ln + stride - 1) // stride).sum())
+    dev = logits.device
+    if out is None:
+        out = (torch.empty(max(num_positions, 1), dtype=torch.int32, device=dev),
+               torch.empty(max(num_positions, 1), dtype=torch.int32, device=dev),
+               torch.empty(max(s, 1), dtype=torch.int32, device=dev))
+    am, tok, cnt = out
+    if workspace is None:
+        workspace = torch.empty(lib.gs_bpe_ctc_workspace_bytes(s, num_positions),
+                                dtype=torch.uint8, device=dev)
+    _check(lib.gs_bpe_pool_ctc_greedy(
+        _dev(logits, "logits", torch.bfloat16), int(ld), _dev(blank_prob, "blank_prob", torch.float32),
+        _dev(cu_seqlens, "cu_seqlens"), s, int(n), int(num_classes), int(window), int(stride),
+        int(num_positions), _dev(am, "argmax", torch.int32), _dev(tok, "tokens", torch.int32),
+        _dev(cnt, "token_counts", torch.int32), workspace.data_ptr(), int(workspace.numel()),
+        _stream(stream)))
+    return am[:num_positions], tok[:num_positions], cnt[:s]
 
 
 def qkv_proj(x: torch.Tensor, wqkv: torch.Tensor, qkv: Optional[torch.Tensor] = None, stream=None):

@@ -257,3 +257,29 @@ def build_xattn_case(w: XattnWorkload, lengths=None) -> XattnCase:
 
 
 XATTN_WORKLOADS = {"bf16_qformer_xattn_b128": XattnWorkload("bf16_qformer_xattn_b128")}
+
+
+# Posterior-weighted pooling + CTC greedy decoding of the BPE head (IBM model
+# card, "Model Architecture" (1); Q4 export README, "Inference note"): logits
+# over 100 353 classes (blank at 0) for the headline batch's frames, rows
+# padded to 100 360 columns (16-byte rows).  The logits are too large to draw
+# on the host (11 GB), so they come from torch's seeded device generator
+# (Philox), N(0, 1) in bf16 with the blank class raised by 2 (most positions
+# decode to blank, as in speech); blank probabilities U(0, 1) in fp32 from
+# the same generator.  Both sides read the same device values.
+BPE_CLASSES = 100353
+BPE_LD = 100360
+
+
+def bpe_inputs(lengths, classes: int = BPE_CLASSES, ld: int = BPE_LD, seed: int = 0,
+               device="cuda"):
+    """(logits [N, ld] bf16, blank_prob [N] fp32, cu_seqlens [S+1] int32) on `device`."""
+    cu = cu_seqlens(lengths)
+    n = int(cu[-1])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    logits = torch.randn((n, ld), generator=g, device=device, dtype=torch.float32)
+    logits[:, 0] += 2.0
+    logits = logits.to(torch.bfloat16)
+    blank = torch.rand((n,), generator=g, device=device, dtype=torch.float32)
+    return logits, blank, torch.from_numpy(cu).to(device)

@@ -207,6 +207,40 @@ gs_status gs_window_xattn_fwd(const void* hcat, const int32_t* cu_seqlens, const
                               int32_t window_frames, int32_t heads, void* out,
                               hipStream_t stream, const gs_xattn_desc* desc);
 
+/*
+ * The BPE head's posterior-weighted pooling and CTC greedy decoding (IBM
+ * model card, "Model Architecture" (1): the BPE head pools windows of 4
+ * frames weighted by 1 - blank probability; ONNX export README, "Parity":
+ * 211 positions for 422 frames, i.e. stride 2; Q4 export README,
+ * "Inference note (NAR decode)": 100353 classes, blank 0, argmax, merge
+ * repeats, drop blanks, token = class - 1).  For each sequence of T frames,
+ * position j = 0 .. ceil(T / stride) - 1 pools frames stride*j ..
+ * min(stride*j + window, T) - 1; class c scores sum_t w_t * logit[t][c] with
+ * w_t = 1 - blank_prob[t], frames in order, every product and partial sum
+ * rounded to fp32 without fused multiply-add (the positive normaliser
+ * 1 / sum w_t changes no argmax and is left out).  argmax[p] = the best
+ * class of position p (ties to the lowest index); then per sequence the kept
+ * classes (not blank, not equal to the previous position's) minus one are
+ * written to tokens[first position of the sequence ...] and their number to
+ * token_counts[s].
+ *   logits       [N][ld] bf16, ld >= num_classes, ld % 8 == 0 (16-byte rows)
+ *   blank_prob   [N] fp32
+ *   cu_seqlens   [S+1] int32 (device), as for gs_block_mhsa_fwd
+ *   num_positions P = sum_s ceil(len_s / stride) (a smaller P drops the
+ *                positions past it; a larger one gets class 0 there)
+ *   argmax, tokens [P] int32, token_counts [S] int32 (device outputs)
+ *   workspace    >= gs_bpe_ctc_workspace_bytes(S, P) bytes, 256-byte aligned
+ * Supported: 1 <= window <= 8, 1 <= stride.
+ */
+size_t gs_bpe_ctc_workspace_bytes(int32_t num_seqs, int32_t num_positions);
+
+gs_status gs_bpe_pool_ctc_greedy(const void* logits, int64_t ld, const float* blank_prob,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int64_t total_frames, int32_t num_classes, int32_t window,
+                                 int32_t stride, int32_t num_positions, int32_t* argmax,
+                                 int32_t* tokens, int32_t* token_counts, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* gs_status_string(gs_status s);
 

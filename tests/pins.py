@@ -406,4 +406,77 @@ def pin_window_xattn_closed_forms(orc):
     assert not np.allclose(moved[1], base[1])
 
 
+def read_ctc_golden(name="ctc_pool_small.txt"):
+    """(classes, lengths, blank_prob, logits, argmax, tokens per sequence) of a fixture."""
+    rows, argmax, tokens = [], None, {}
+    classes = lengths = None
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        if line.startswith("classes"):
+            classes = int(line.split()[1])
+        elif line.startswith("lengths"):
+            lengths = [int(v) for v in line.split()[1:]]
+        elif line.startswith("argmax"):
+            argmax = [int(v) for v in line.split()[1:]]
+        elif line.startswith("tokens"):
+            k, v = line[len("tokens"):].split(":")
+            tokens[int(k)] = [int(t) for t in v.split()]
+        else:
+            rows.append([float(v) for v in line.split()])
+    rows = np.asarray(rows)
+    assert rows.shape == (sum(lengths), classes + 1)
+    return classes, lengths, rows[:, 0], rows[:, 1:], argmax, [tokens[i] for i in range(len(lengths))]
+
+
+def pin_ctc_pool_golden(orc):
+    """The hand-worked fixture: window 4, stride 2, weights 1 - blank
+    probability, ties to the lowest class, merge, drop blanks, minus one."""
+    from oracle import ctc_pool as cp
+    classes, lengths, bp, logits, argmax, tokens = read_ctc_golden()
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    got = cp.pooled_argmax(logits, bp, cu)
+    assert got.tolist() == argmax
+    dec = cp.ctc_greedy(got, cp.positions(lengths))
+    assert [t.tolist() for t in dec] == tokens
+
+
+def pin_ctc_pool_constructed(orc):
+    """Decoding recovers token sequences that the inputs were built from: each
+    token becomes one or more pooled positions (repeats), with blanks between
+    equal neighbours and at random; every frame pair of position j carries its
+    class with a margin over noise, and pair weights halve along the sequence
+    (1 - blank probability = 2^-j) so each pooled window is won by its first
+    pair."""
+    from oracle import ctc_pool as cp
+    rng = np.random.default_rng(21)
+    classes = 40
+    want, logits, bp, lengths = [], [], [], []
+    for _ in range(5):
+        toks = rng.integers(0, classes - 1, size=int(rng.integers(0, 7)))
+        seq = []  # winning class per position
+        for i, t in enumerate(toks):
+            if seq and (seq[-1] == t + 1 or rng.random() < 0.4):
+                seq.append(0)
+            seq += [int(t) + 1] * int(rng.integers(1, 3))
+        seq += [0] * int(rng.integers(0, 2))
+        if len(seq) > 24:
+            continue
+        n = 2 * len(seq) - int(rng.integers(0, 2)) if seq else 0  # odd lengths too
+        for t in range(n):
+            j = t // 2
+            row = rng.uniform(-1, 1, classes)
+            row[seq[j]] += 20.0
+            logits.append(row)
+            bp.append(1.0 - 2.0 ** -j)
+        lengths.append(n)
+        want.append([int(t) for t in toks])
+    logits = np.asarray(logits, np.float32).reshape(-1, classes)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    ids = cp.pooled_argmax(logits, np.asarray(bp, np.float32), cu)
+    got = cp.ctc_greedy(ids, cp.positions(lengths))
+    assert [g.tolist() for g in got] == want, (got, want)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
