@@ -19,7 +19,9 @@
 //     workgroup per PA_POS consecutive positions; thread i scores classes
 //     8i + 2048k .. +7 (16-byte loads of bf16 logits) for each of its
 //     positions, keeps a running (max, index) per position, and the
-//     workgroup reduces them at the end;
+//     workgroup reduces them at the end.  With window 4 and stride 2 and
+//     positions of one sequence, each frame is loaded once and serves the
+//     two windows that hold it;
 //   * decode: one wave per sequence, 64 positions at a time, ballot and
 //     prefix count to compact the kept tokens.
 #include "gs_device.hpp"
@@ -77,7 +79,8 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 // logits [N][ld] bf16 (ld % 8 == 0, ld >= C), blank_prob [N] fp32.
 __global__ __launch_bounds__(PA_THREADS) void pooled_argmax_kernel(
     const bf16* __restrict__ logits, long long ld, const float* __restrict__ blank_prob,
-    const int4* __restrict__ table, int P, int C, int* __restrict__ argmax) {
+    const int4* __restrict__ table, int P, int C, int stride, int window,
+    int* __restrict__ argmax) {
   // every product and sum rounded on its own (the argmax must not depend on
   // contraction into fused multiply-adds)
 #pragma clang fp contract(off)
@@ -104,31 +107,58 @@ __global__ __launch_bounds__(PA_THREADS) void pooled_argmax_kernel(
     bv[r] = -INFINITY;
     bi[r] = 0x7fffffff;
   }
-  for (int c0 = 8 * tid; c0 < C; c0 += 8 * PA_THREADS) {
+  // the scores of position r for classes c0 .. c0+7 from its frames' 16-byte
+  // pieces (frames in order), folded into the running maximum
+  auto score = [&](int r, int c0, auto piece) __attribute__((always_inline)) {
+    float acc[8];
 #pragma unroll
-    for (int r = 0; r < PA_POS; ++r) {
-      float acc[8];
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+    for (int f = 0; f < PA_MAXWIN; ++f) {
+      if (f < nt[r]) {
+        const u32x4_t u = piece(r, f);
 #pragma unroll
-      for (int f = 0; f < PA_MAXWIN; ++f) {
-        if (f < nt[r]) {
-          const u32x4_t u = *(const u32x4_t*)(logits + (size_t)(t0[r] + f) * ld + c0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float lo = __builtin_bit_cast(float, u[e] << 16);
-            const float hi = __builtin_bit_cast(float, u[e] & 0xFFFF0000u);
-            acc[2 * e] = acc[2 * e] + w[r][f] * lo;
-            acc[2 * e + 1] = acc[2 * e + 1] + w[r][f] * hi;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __builtin_bit_cast(float, u[e] << 16);
+          const float hi = __builtin_bit_cast(float, u[e] & 0xFFFF0000u);
+          acc[2 * e] = acc[2 * e] + w[r][f] * lo;
+          acc[2 * e + 1] = acc[2 * e + 1] + w[r][f] * hi;
         }
       }
+    }
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (c0 + k < C && acc[k] > bv[r]) {  // classes rise within a thread: '>' keeps the first
-          bv[r] = acc[k];
-          bi[r] = c0 + k;
-        }
+    for (int k = 0; k < 8; ++k)
+      if (c0 + k < C && acc[k] > bv[r]) {  // classes rise within a thread: '>' keeps the first
+        bv[r] = acc[k];
+        bi[r] = c0 + k;
+      }
+  };
+  // Window 4, stride 2, the workgroup's positions consecutive in one
+  // sequence: their windows cover 2 (PA_POS - 1) + 4 consecutive frames, each
+  // loaded once and shared by the two positions whose windows hold it.
+  constexpr int FROWS = 2 * (PA_POS - 1) + 4;
+  bool shared_rows = stride == 2 && window == 4;
+#pragma unroll
+  for (int r = 1; r < PA_POS; ++r) shared_rows = shared_rows && t0[r] == t0[0] + 2 * r;
+  if (shared_rows) {
+    const int nrows = 2 * (PA_POS - 1) + nt[PA_POS - 1];  // frames the last window reaches
+    for (int c0 = 8 * tid; c0 < C; c0 += 8 * PA_THREADS) {
+      u32x4_t u[FROWS];
+#pragma unroll
+      for (int i = 0; i < FROWS; ++i)
+        u[i] = i < nrows ? *(const u32x4_t*)(logits + (size_t)(t0[0] + i) * ld + c0)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < PA_POS; ++r)
+        score(r, c0, [&](int rr, int f) { return u[2 * rr + f < FROWS ? 2 * rr + f : 0]; });
+    }
+  } else {
+    for (int c0 = 8 * tid; c0 < C; c0 += 8 * PA_THREADS) {
+#pragma unroll
+      for (int r = 0; r < PA_POS; ++r)
+        score(r, c0, [&](int rr, int f) {
+          return *(const u32x4_t*)(logits + (size_t)(t0[rr] + f) * ld + c0);
+        });
     }
   }
   // reduce (max, lowest index) over the wave, then over the waves
@@ -203,7 +233,7 @@ hipError_t launch_bpe_pool_ctc(const void* logits, long long ld, const float* bl
   if (P > 0) {
     hipLaunchKernelGGL(pooled_argmax_kernel, dim3((P + PA_POS - 1) / PA_POS), dim3(PA_THREADS), 0,
                        stream, (const bf16*)logits, ld, blank_prob, (const int4*)table, P, C,
-                       argmax);
+                       stride, window, argmax);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
