@@ -105,3 +105,27 @@ def test_ctc_pool_full_size_sampled():
         want = cp.ctc_greedy(ref, [len(ref)])[0].tolist()
         assert tok[first[s]:first[s] + cnt[s]].tolist() == want, s
     print(f"  positions={int(first[-1])} tokens={int(cnt.sum())}", flush=True)
+
+
+def test_ctc_pool_num_positions_past_the_count():
+    """A num_positions above the sequences' count: the extra positions get
+    class 0 and every sequence's tokens are unchanged."""
+    rng = np.random.default_rng(8)
+    classes, lengths = 256, [9, 4, 0, 13]
+    n = sum(lengths)
+    logits = torch.from_numpy(rng.standard_normal((n, classes)).astype(np.float32)).to(
+        torch.bfloat16)
+    bp = torch.from_numpy(rng.uniform(0, 1, n).astype(np.float32))
+    dev = G.dev()
+    cu = torch.from_numpy(workloads.cu_seqlens(lengths)).to(dev)
+    p = int(cp.positions(lengths).sum())
+    a1, t1, c1 = gsattn.bpe_pool_ctc_greedy(logits.to(dev), bp.to(dev), cu, classes)
+    a2, t2, c2 = gsattn.bpe_pool_ctc_greedy(logits.to(dev), bp.to(dev), cu, classes,
+                                            num_positions=p + 3)
+    torch.cuda.synchronize()
+    assert torch.equal(a2[:p], a1) and a2[p:].tolist() == [0, 0, 0]
+    assert torch.equal(c2, c1)
+    t1, t2, c1 = t1.cpu().numpy(), t2.cpu().numpy(), c1.cpu().numpy()
+    first = np.concatenate([[0], np.cumsum(cp.positions(lengths))])
+    for s in range(len(lengths)):
+        assert np.array_equal(t2[first[s]:first[s] + c1[s]], t1[first[s]:first[s] + c1[s]])

@@ -342,6 +342,21 @@ def test_padded_garbage_in_padding_does_not_leak():
     assert torch.equal(out2.reshape(-1, d)[~vt], x2[~vt])
 
 
+def test_padded_lengths_outside_the_bucket_are_clamped():
+    """Lengths below 0 or above the bucket act as 0 and T (the documented
+    clamp), bit for bit."""
+    t, block, d, heads = 96, 64, 256, 2
+    G.print_case("padded clamp", T=t)
+    case, x, lens, wqkv, wo, out, valid = _padded_run([-3, 96, 40], t, block, d, heads,
+                                                      torch.bfloat16, seed=12)
+    lens2 = torch.tensor([0, t, 40], dtype=torch.int32, device=G.dev())
+    out_big = gsattn.block_mhsa_fwd_padded(x, torch.tensor([0, t + 5, 40], dtype=torch.int32,
+                                                           device=G.dev()), wqkv, wo, block, heads)
+    out_ref = gsattn.block_mhsa_fwd_padded(x, lens2, wqkv, wo, block, heads)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref) and torch.equal(out_big, out_ref)
+
+
 def test_padded_bucket_workload_sampled(orc):
     """128 buckets of 800 rows holding the headline batch's lengths capped at
     800, as the benchmark runs them: sampled buckets against the oracle,

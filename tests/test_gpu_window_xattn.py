@@ -97,3 +97,19 @@ def test_window_xattn_full_size_sampled():
                                   c.wo.to(dev), c.window_frames, c.heads)
     torch.cuda.synchronize()
     assert torch.equal(one, out[w0:w1]), "a sequence run alone differs"
+
+
+def test_window_xattn_debug_check_rejects_a_wrong_window_count(monkeypatch):
+    """Under GSATTN_DEBUG_CHECKS=1 a num_windows that is not the sequences'
+    count is rejected before any projection runs."""
+    monkeypatch.setenv("GSATTN_DEBUG_CHECKS", "1")
+    c = _small([31, 15], 15, 3, 256, 256, 2, seed=2)   # 3 + 1 = 4 windows
+    dev = G.dev()
+    xq = torch.cat([c.xq, c.xq[:1]]).to(dev)            # 5 windows of query states
+    with pytest.raises(gsattn.GsError) as e:
+        gsattn.window_xattn_fwd(c.hcat.to(dev), torch.from_numpy(c.cu).to(dev), xq,
+                                c.wq.to(dev), c.wkv.to(dev), c.wo.to(dev), c.window_frames,
+                                c.heads)
+    assert "num_windows" in str(e.value)
+    out = _run(c)  # the right count passes the check
+    assert out.shape == c.xq.shape
