@@ -329,7 +329,12 @@ def main():
     weights = [(a.to(dev), b.to(dev)) for a, b in case.weights]
     n, d = x.shape
     nl = len(weights)
-    ws = gsattn.alloc_workspace(n, d, x.dtype, dev)
+    if case.bucket_frames:
+        nb = gsattn.load().gs_block_mhsa_padded_workspace_bytes(
+            len(case.lengths), case.bucket_frames, d, gsattn._gs_dtype(x.dtype))
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    else:
+        ws = gsattn.alloc_workspace(n, d, x.dtype, dev)
     bufs = [torch.empty_like(x), torch.empty_like(x)]
     stream = torch.cuda.current_stream()
 

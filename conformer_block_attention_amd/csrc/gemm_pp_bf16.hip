@@ -132,12 +132,15 @@ __device__ __forceinline__ void swap_lo_hi(unsigned& x, unsigned& y) {
 }  // namespace pp
 
 // KK: 16-wide k chunks per phase (a stage of 64 k takes 4 / KK phases per
-// group).
+// group).  m_dev: if not null, the row count is read from device memory
+// instead of M (M then only bounds the grid), for row counts that exist only
+// on the device.
 template <int BN, bool RESID, int KK>
 __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* R, bf16* C, int M,
-    int Nc, int K) {
+    int Nc, int K, const int* __restrict__ m_dev) {
   using namespace pp;
+  if (m_dev) M = __builtin_amdgcn_readfirstlane(*m_dev);
   using CopyA = Copy<BM, true>;   // activation rows: the last panel is ragged
   using CopyB = Copy<BN, false>;  // weight rows: Nc % BN == 0
   constexpr int WN = BN / 4;      // wave tile columns
@@ -439,17 +442,22 @@ static int pp_split_rows(int M, int tiles_per_panel) {
 // C[r0 .. r0+rows) for one part of the row split (RESID: out_proj).
 template <int BN, bool RESID>
 static void pp_launch_part(const bf16* A, const bf16* W, const bf16* R, bf16* C, int r0, int rows,
-                           int Nc, int K, hipStream_t stream) {
+                           int Nc, int K, hipStream_t stream, const int* m_dev = nullptr) {
   const int mt = (rows + pp::BM - 1) / pp::BM;
   const size_t a_off = (size_t)r0 * K, c_off = (size_t)r0 * Nc;
   hipLaunchKernelGGL((gemm_pp_bf16_kernel<BN, RESID, 2>), dim3(pp_persistent_grid(mt * (Nc / BN))),
                      dim3(pp::THREADS), 0, stream, A + a_off, W, RESID ? R + c_off : R, C + c_off,
-                     rows, Nc, K);
+                     rows, Nc, K, m_dev);
 }
 
+// m_dev (optional): the row count on the device, at most M; one launch then.
 template <bool RESID>
 static hipError_t pp_launch(const bf16* A, const bf16* W, const bf16* R, bf16* C, int M, int Nc,
-                            int K, hipStream_t stream) {
+                            int K, hipStream_t stream, const int* m_dev = nullptr) {
+  if (m_dev) {
+    pp_launch_part<256, RESID>(A, W, R, C, 0, M, Nc, K, stream, m_dev);
+    return hipGetLastError();
+  }
   const int m1 = pp_split_rows(M, Nc / 256);
   pp_launch_part<256, RESID>(A, W, R, C, 0, m1, Nc, K, stream);
   if (m1 < M) {
@@ -475,12 +483,14 @@ hipError_t launch_out_proj_bf16_pp(const void* o, const void* wo, const void* x,
 
 // C[M][Nc] = A[M][K] . W[Nc][K]^T (+ R[M][Nc] when R is not null), for any
 // Nc % 256 == 0 and K % 64 == 0 (the window cross-attention's projections).
+// m_dev (optional): rows counted on the device (at most M).
 hipError_t launch_gemm_nt_bf16_pp(const void* A, const void* W, const void* R, void* C, int M,
-                                  int Nc, int K, hipStream_t stream) {
+                                  int Nc, int K, hipStream_t stream, const int* m_dev) {
   if (R)
     return pp_launch<true>((const bf16*)A, (const bf16*)W, (const bf16*)R, (bf16*)C, M, Nc, K,
-                           stream);
-  return pp_launch<false>((const bf16*)A, (const bf16*)W, nullptr, (bf16*)C, M, Nc, K, stream);
+                           stream, m_dev);
+  return pp_launch<false>((const bf16*)A, (const bf16*)W, nullptr, (bf16*)C, M, Nc, K, stream,
+                          m_dev);
 }
 
 }  // namespace gs

@@ -28,7 +28,7 @@ hipError_t launch_bpe_pool_ctc(const void* logits, long long ld, const float* bl
                                int* argmax, int* tokens, int* counts, void* workspace,
                                hipStream_t stream);
 hipError_t launch_gemm_nt_bf16_pp(const void* A, const void* W, const void* R, void* C, int M,
-                                  int Nc, int K, hipStream_t stream);
+                                  int Nc, int K, hipStream_t stream, const int* m_dev = nullptr);
 hipError_t launch_window_attn_bf16(const void* kv, const void* q, const int* cu, int S, int W,
                                    int nq, int heads, int dq, int window, void* table,
                                    void* o, hipStream_t stream);
@@ -74,6 +74,71 @@ __global__ __launch_bounds__(256) void zero_pad_rows_kernel(const int* len, int 
   for (int t = max(t0, l); t < t1; ++t) {
     uint4* row = o + ((size_t)b * T + t) * pieces;
     for (int i = threadIdx.x; i < pieces; i += blockDim.x) row[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+// cu[0] = 0, cu[b + 1] = cu[b] + (len[b] clamped to [0, T]).  One workgroup.
+__global__ __launch_bounds__(1024) void lengths_prefix_kernel(const int* __restrict__ len, int S,
+                                                             int T, int* __restrict__ cu) {
+  __shared__ int scan[1024];
+  __shared__ int base;
+  const int tid = threadIdx.x;
+  if (tid == 0) base = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < S; c0 += 1024) {
+    const int b = c0 + tid;
+    int l = b < S ? len[b] : 0;
+    l = l < 0 ? 0 : (l > T ? T : l);
+    scan[tid] = l;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int y = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += y;
+      __syncthreads();
+    }
+    if (b < S) cu[b + 1] = base + scan[tid];
+    __syncthreads();
+    if (tid == 1023) base += scan[1023];
+    __syncthreads();
+  }
+  if (tid == 0) cu[0] = 0;
+}
+
+// Valid rows of the buckets, packed: xp[cu[b] + t] = x[b*T + t], t < len[b].
+// Grid (ceil(T / ZP_ROWS), S); rows of `pieces` 16-byte pieces.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                          const int* __restrict__ len,
+                                                          const int* __restrict__ cu, int T,
+                                                          int pieces, uint4* __restrict__ xp) {
+  const int b = blockIdx.y;
+  int l = len[b];
+  l = l < 0 ? 0 : (l > T ? T : l);
+  const int t0 = blockIdx.x * ZP_ROWS;
+  const int t1 = min(t0 + ZP_ROWS, l);
+  for (int t = t0; t < t1; ++t) {
+    const uint4* src = x + ((size_t)b * T + t) * pieces;
+    uint4* dst = xp + ((size_t)cu[b] + t) * pieces;
+    for (int i = threadIdx.x; i < pieces; i += blockDim.x) dst[i] = src[i];
+  }
+}
+
+// out[b*T + t] = outp[cu[b] + t] for t < len[b], x[b*T + t] for padding rows.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restrict__ outp,
+                                                           const uint4* x,
+                                                           const int* __restrict__ len,
+                                                           const int* __restrict__ cu, int T,
+                                                           int pieces, uint4* out) {
+  const int b = blockIdx.y;
+  int l = len[b];
+  l = l < 0 ? 0 : (l > T ? T : l);
+  const int t0 = blockIdx.x * ZP_ROWS;
+  const int t1 = min(t0 + ZP_ROWS, T);
+  for (int t = t0; t < t1; ++t) {
+    const size_t row = (size_t)b * T + t;
+    const uint4* src = t < l ? outp + ((size_t)cu[b] + t) * pieces : x + row * pieces;
+    uint4* dst = out + row * pieces;
+    if (src == dst) continue;  // (in place, padding row)
+    for (int i = threadIdx.x; i < pieces; i += blockDim.x) dst[i] = src[i];
   }
 }
 }  // namespace gs
@@ -354,12 +419,30 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
   return GS_OK;
 }
 
+size_t gs_block_mhsa_padded_workspace_bytes(int32_t num_seqs, int32_t bucket_frames,
+                                            int32_t d_model, gs_dtype dtype) {
+  if (num_seqs < 1 || bucket_frames < 1) return 0;
+  const int64_t rows = (int64_t)num_seqs * bucket_frames;
+  const size_t base = gs_block_mhsa_workspace_bytes(rows, d_model, dtype);
+  if (base == 0) return 0;
+  // the valid rows packed (input and output) and their offsets
+  const size_t packed = align_up((size_t)rows * d_model * elem_size(dtype));
+  return base + 2 * packed + align_up(4 * ((size_t)num_seqs + 1));
+}
+
 gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_t bucket_frames,
                                    const void* Wqkv, const void* Wo, int32_t block_frames,
                                    int32_t heads, void* out, hipStream_t stream,
                                    const gs_mhsa_desc* desc) {
   FwdPlan p{};
   GS_TRY(plan_fwd(x, Wqkv, Wo, block_frames, heads, out, desc, p));
+  if (desc && p.N > 0 && bucket_frames >= 1 && desc->num_seqs >= 1) {
+    const size_t need = gs_block_mhsa_padded_workspace_bytes(desc->num_seqs, bucket_frames, p.d,
+                                                             desc->dtype);
+    if (desc->workspace_bytes < need)
+      return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                  desc->workspace_bytes, need);
+  }
   if (!lengths) return fail(GS_ERR_INVALID_ARGUMENT, "lengths is NULL");
   if (bucket_frames < 1) return fail(GS_ERR_INVALID_ARGUMENT, "bucket_frames %d < 1", bucket_frames);
   if ((int64_t)desc->num_seqs * bucket_frames != p.N)
@@ -368,16 +451,50 @@ gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_
   if (p.N == 0) return GS_OK;
   GS_TRY(debug_check_lengths(lengths, desc->num_seqs, bucket_frames, p.dflag, stream));
   const size_t e = elem_size(desc->dtype);
+  const dim3 rows_grid((bucket_frames + gs::ZP_ROWS - 1) / gs::ZP_ROWS, desc->num_seqs);
+  const int pieces = (int)((size_t)p.d * e / 16);
+
+  if (desc->dtype == GS_BF16 && p.d % 256 == 0) {
+    // Compact: pack the valid rows, run the packed sub-layer on them with
+    // the row count taken on the device, and unpack (padding rows copy x).
+    char* ws = (char*)desc->workspace + gs_block_mhsa_workspace_bytes(p.N, p.d, desc->dtype);
+    const size_t packed = align_up((size_t)p.N * p.d * e);
+    void* xp = ws;
+    void* outp = ws + packed;
+    int* cu = (int*)(ws + 2 * packed);
+    const int S = desc->num_seqs;
+    GS_TRY(record(desc, 0, stream));
+    hipLaunchKernelGGL(gs::lengths_prefix_kernel, dim3(1), dim3(1024), 0, stream,
+                       (const int*)lengths, S, (int)bucket_frames, cu);
+    hipLaunchKernelGGL(gs::gather_rows_kernel, rows_grid, dim3(256), 0, stream, (const uint4*)x,
+                       (const int*)lengths, (const int*)cu, (int)bucket_frames, pieces,
+                       (uint4*)xp);
+    GS_TRY(hip_status(hipGetLastError(), "row packing launch"));
+    GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp(xp, Wqkv, nullptr, p.qkv, (int)p.N, 3 * p.d, p.d,
+                                                 stream, cu + S),
+                      "qkv_proj launch"));
+    GS_TRY(record(desc, 1, stream));
+    GS_TRY(attn_spans(p.qkv, gs::SeqSpans{cu, 0}, S, p.N, p.d, heads, block_frames, desc->dtype,
+                      p.o, p.table, stream));
+    GS_TRY(record(desc, 2, stream));
+    GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp(p.o, Wo, xp, outp, (int)p.N, p.d, p.d, stream,
+                                                 cu + S),
+                      "out_proj launch"));
+    hipLaunchKernelGGL(gs::scatter_rows_kernel, rows_grid, dim3(256), 0, stream,
+                       (const uint4*)outp, (const uint4*)x, (const int*)lengths, (const int*)cu,
+                       (int)bucket_frames, pieces, (uint4*)out);
+    GS_TRY(hip_status(hipGetLastError(), "row unpacking launch"));
+    GS_TRY(record(desc, 3, stream));
+    return GS_OK;
+  }
 
   GS_TRY(record(desc, 0, stream));
   GS_TRY(gs_qkv_proj(x, Wqkv, p.qkv, p.N, p.d, desc->dtype, stream));
   GS_TRY(record(desc, 1, stream));
   GS_TRY(attn_spans(p.qkv, gs::SeqSpans{lengths, bucket_frames}, desc->num_seqs, p.N, p.d, heads,
                     block_frames, desc->dtype, p.o, p.table, stream));
-  hipLaunchKernelGGL(gs::zero_pad_rows_kernel,
-                     dim3((bucket_frames + gs::ZP_ROWS - 1) / gs::ZP_ROWS, desc->num_seqs),
-                     dim3(256), 0, stream, (const int*)lengths, (int)bucket_frames,
-                     (int)((size_t)p.d * e / 16), (uint4*)p.o);
+  hipLaunchKernelGGL(gs::zero_pad_rows_kernel, rows_grid, dim3(256), 0, stream,
+                     (const int*)lengths, (int)bucket_frames, pieces, (uint4*)p.o);
   GS_TRY(hip_status(hipGetLastError(), "padding rows launch"));
   GS_TRY(record(desc, 2, stream));
   GS_TRY(gs_out_proj_residual(p.o, Wo, x, out, p.N, p.d, desc->dtype, stream));

@@ -21,6 +21,7 @@ GS_F32, GS_BF16 = 0, 1
 
 EXPORTS = (
     "gs_block_mhsa_workspace_bytes", "gs_block_mhsa_fwd", "gs_block_mhsa_fwd_padded",
+    "gs_block_mhsa_padded_workspace_bytes",
     "gs_qkv_proj", "gs_block_attn",
     "gs_block_attn_workspace_bytes", "gs_out_proj_residual", "gs_status_string",
     "gs_last_error_detail", "gs_version", "gs_window_xattn_workspace_bytes",
@@ -80,6 +81,8 @@ def load(path: Optional[str] = None):
     lib.gs_block_mhsa_workspace_bytes.argtypes = [I64, I32, ctypes.c_int]
     lib.gs_block_mhsa_fwd.restype = ctypes.c_int
     lib.gs_block_mhsa_fwd.argtypes = [P, P, P, P, I32, I32, P, P, ctypes.POINTER(_Desc)]
+    lib.gs_block_mhsa_padded_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_block_mhsa_padded_workspace_bytes.argtypes = [I32, I32, I32, ctypes.c_int]
     lib.gs_block_mhsa_fwd_padded.restype = ctypes.c_int
     lib.gs_block_mhsa_fwd_padded.argtypes = [P, P, I32, P, P, I32, I32, P, P,
                                              ctypes.POINTER(_Desc)]
@@ -190,7 +193,8 @@ def block_mhsa_fwd_padded(x: torch.Tensor, lengths: torch.Tensor, wqkv: torch.Te
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
-        workspace = alloc_workspace(s * t, d, x.dtype, x.device)
+        workspace = torch.empty(max(lib.gs_block_mhsa_padded_workspace_bytes(s, t, d, dt), 1),
+                                dtype=torch.uint8, device=x.device)
     if lengths.dtype != torch.int32 or lengths.numel() != s:
         raise TypeError("lengths must be int32 with one entry per bucket")
     desc = _Desc(int(s), int(s * t), int(d), dt, workspace.data_ptr(), int(workspace.numel()),

@@ -117,10 +117,16 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
  * Blocks restart at each bucket's first row and never include padding rows,
  * so the valid rows of `out` equal those of gs_block_mhsa_fwd on the same
  * sequences packed.  Padding rows are neither queries nor keys: their
- * attention output is zero, so out = x there (up to the sign of zero).  The
- * projections run over all S*T rows; the workspace is that of
- * gs_block_mhsa_workspace_bytes(S*T, d, dtype).
+ * attention output is zero, so out = x there (up to the sign of zero).  For
+ * bf16 with d a multiple of 256 the valid rows are packed on the device,
+ * run through the packed sub-layer (the projections take the row count from
+ * device memory) and unpacked; otherwise the projections run over all S*T
+ * rows and O's padding rows are zeroed.  The workspace is
+ * gs_block_mhsa_padded_workspace_bytes(S, T, d, dtype) bytes.
  */
+size_t gs_block_mhsa_padded_workspace_bytes(int32_t num_seqs, int32_t bucket_frames,
+                                            int32_t d_model, gs_dtype dtype);
+
 gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_t bucket_frames,
                                    const void* Wqkv, const void* Wo, int32_t block_frames,
                                    int32_t heads, void* out, hipStream_t stream,
