@@ -34,9 +34,10 @@ constexpr int PA_THREADS = 256;
 constexpr int PA_POS = 4;       // positions per workgroup
 constexpr int PA_MAXWIN = 8;    // frames per pooling window
 
-// table[p] = {first frame, frames, sequence, 0} for the positions the
-// sequences make (in order; entries up to P past that count hold frames 0);
-// pos_cu[s] = first position of sequence s, pos_cu[S] = that count.
+// pos_cu[s] = first position of sequence s, pos_cu[S] = the number of
+// positions the sequences make.  (The table of positions, {first frame,
+// frames, sequence, 0} in order, with frames 0 for entries from that count
+// up to P, is filled by the next kernel.)
 __global__ __launch_bounds__(1024) void build_position_table_kernel(
     const int* __restrict__ cu, int S, int window, int stride, int P, int4* __restrict__ table,
     int* __restrict__ pos_cu) {
@@ -60,16 +61,33 @@ __global__ __launch_bounds__(1024) void build_position_table_kernel(
     }
     const int first = base + scan[tid] - n;
     if (s < S) pos_cu[s] = first;
-    for (int j = 0; j < n; ++j) {
-      const int p = first + j;
-      if (p < P) table[p] = make_int4(start + j * stride, min(window, len - j * stride), s, 0);
-    }
+    (void)start;
     __syncthreads();
     if (tid == 1023) base += scan[1023];
     __syncthreads();
   }
-  for (int p = base + tid; p < P; p += 1024) table[p] = make_int4(0, 0, 0, 0);
   if (tid == 0) pos_cu[S] = base;
+}
+
+// table[p] for every position p < P: its sequence by binary search in
+// pos_cu, then its first frame and frame count.
+__global__ __launch_bounds__(256) void fill_position_table_kernel(
+    const int* __restrict__ cu, const int* __restrict__ pos_cu, int S, int window, int stride,
+    int P, int4* __restrict__ table) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= P) return;
+  if (p >= pos_cu[S]) {  // past the positions the sequences make
+    table[p] = make_int4(0, 0, 0, 0);
+    return;
+  }
+  int lo = 0, hi = S - 1;  // the last s with pos_cu[s] <= p (sequences without positions skipped)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pos_cu[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  const int j = p - pos_cu[lo];
+  const int start = cu[lo], len = cu[lo + 1] - start;
+  table[p] = make_int4(start + j * stride, min(window, len - j * stride), lo, 0);
 }
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
@@ -230,6 +248,12 @@ hipError_t launch_bpe_pool_ctc(const void* logits, long long ld, const float* bl
                                                                   pos_cu);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (P > 0) {
+    hipLaunchKernelGGL(fill_position_table_kernel, dim3((P + 255) / 256), dim3(256), 0, stream, cu,
+                       (const int*)pos_cu, S, window, stride, P, table);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (P > 0) {
     hipLaunchKernelGGL(pooled_argmax_kernel, dim3((P + PA_POS - 1) / PA_POS), dim3(PA_THREADS), 0,
                        stream, (const bf16*)logits, ld, blank_prob, (const int4*)table, P, C,
