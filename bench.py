@@ -295,7 +295,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(the sub-layer shards by whole sequences with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
