@@ -30,13 +30,16 @@
 //   * O^T += V^T P^T: the V^T operand is read straight from the row-major V
 //     rows with the transposing LDS read ds_read_b64_tr_b16; the row sums of
 //     P come from the same product with an all-ones operand;
-//   * softmax in base 2 against a per-row reference fixed at the item's first
+//   * softmax in base 2 against a per-row reference set at the item's first
 //     chunk (an integer: the ceiling of that chunk's row max); later scores
-//     may exceed it by any amount: P then carries an exact power-of-two
-//     factor, rounds to bf16 as it would against the true max, and cancels in
-//     O = acc / sum.  Only a P, sum or accumulator that overflows can break
-//     that; an item whose row sums or accumulators end non-finite is flagged
-//     and recomputed exactly at the end of the kernel;
+//     may exceed it: P then carries an exact power-of-two factor, rounds to
+//     bf16 as it would against the true max, and cancels in O = acc / sum.
+//     When a chunk's scores run more than 2^32 above a row's reference, the
+//     reference rises to that chunk's ceiling and the accumulated O, sum and
+//     pending P are scaled by the exact power of two between the two (rare
+//     at unit-variance logits, common in deep unnormalised stacks).  An item
+//     whose row sums or accumulators still end non-finite is flagged and
+//     recomputed exactly at the end of the kernel;
 //   * P is rounded to bf16 (RNE) for the MFMA and the sums use the rounded
 //     values; O = acc / sum is rounded once to bf16;
 //   * rows past the block end are copies of its last row (finite data) and
@@ -54,6 +57,7 @@ constexpr int ATT_QT = 2;            // 16-row query tiles per math wave
 constexpr int ATT_QW = 16 * ATT_QT;  // query rows per math wave
 constexpr int ATT_QG = ATT_PRODUCER * ATT_QW;  // query rows per unit (7 waves x 32)
 constexpr int ATT_KC = 32;           // keys per key chunk
+constexpr float ATT_HEADROOM = 32.f;  // log2 margin of a score over its row's reference
 constexpr int DH = 128;
 constexpr int ATT_NST = 8;           // ring stages
 constexpr int ATT_AHEAD = 4;         // copies run this many stages ahead (<= 63 in flight)
@@ -188,10 +192,6 @@ __device__ __forceinline__ float xsum_lanes16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Scores may exceed an item's reference max by this many doublings before the
-// item is handed to the exact fallback: P <= 2^64, and O and the row sums of
-// at most 2^31 keys stay far inside fp32 range for any |V| < 2^32.
-
 // Workgroup barrier without a memory fence.  A fence would make every wave
 // wait for all of its outstanding global->LDS copies and global stores; the
 // stream loop instead waits explicitly for exactly the copies it needs.  This
@@ -300,9 +300,9 @@ __device__ __forceinline__ void swap_row_pairs(unsigned& x, unsigned& y) {
 }
 
 // Exact attention for one item (unit u of the table, head h) whose row sums
-// or accumulators overflowed against the first chunk's reference (its scores
-// ran about 100 doublings or more above it; never seen with logits of
-// ordinary size).  Two passes over the keys per query row: the row
+// or accumulators overflowed against its reference (a chunk's scores ran
+// about 100 doublings or more above it within one chunk of the reference's
+// last rise; never seen with logits of ordinary size).  Two passes over the keys per query row: the row
 // max, then P with the rounding of the fast path (reference = ceil of the row
 // max in log2 units, P rounded to bf16, the sum taken over the rounded values)
 // and O = sum_j P_j V_j / sum_j P_j, rounded once to bf16.  Waves w0, w0 +
@@ -654,12 +654,13 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         constexpr int QT = decltype(qtc)::value;
         f32x4 oacc[QT][8];
         f32x4 lsum[QT];  // P row sums: lsum[tt] += 1 * P^T (4 copies per lane)
-        // Reference max per query: an integer in log2 units, fixed at the item's
-        // first chunk to ceil(that chunk's row max).  Later scores may exceed it:
-        // with an integer reference P differs from P against the true row max
-        // by an exact power of two, so it rounds to bf16 the same way and the
-        // factor cancels in acc / sum, unless something overflows (checked at
-        // the end of the item).
+        // Reference max per query: an integer in log2 units, set at the item's
+        // first chunk to ceil(that chunk's row max) and raised when a later
+        // chunk runs far above it.  Later scores may exceed it: with an
+        // integer reference P differs from P against the true row max by an
+        // exact power of two, so it rounds to bf16 the same way and the factor
+        // cancels in acc / sum, unless something overflows (checked at the end
+        // of the item).
         float mref[QT];
         bf16x8 pprev[QT];  // P of the previous chunk, whose PV product is pending
         int pslot;
@@ -694,7 +695,37 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           bf16x8 vf[8];
           read_vt(pslot, vf);
           __builtin_amdgcn_sched_barrier(0);
-          mask(qtc, s, min(ATT_KC, L - kc * ATT_KC));
+          // the chunk's row max (masked keys excluded)
+          float lmax[QT];
+          mask_max(qtc, s, min(ATT_KC, L - kc * ATT_KC), lmax);
+          // Lazy rescale: when a row's scores run more than 2^ATT_HEADROOM
+          // above its reference, the reference rises to this chunk's
+          // ceiling and everything accumulated against the old one (O, the
+          // row sum and the pending P) is scaled by the exact power of two
+          // between them.  Rare for unit-variance inputs; frequent in deep
+          // stacks without normalisation, whose logits grow layer by layer.
+          {
+            float mnew[QT];
+            bool grow = false;
+#pragma unroll
+            for (int tt = 0; tt < QT; ++tt) {
+              mnew[tt] = __builtin_ceilf(xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2);
+              grow = grow || mnew[tt] > mref[tt] + ATT_HEADROOM;
+            }
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // (wave-uniform)
+#pragma unroll
+              for (int tt = 0; tt < QT; ++tt) {
+                const float m2 = fmaxf(mref[tt], mnew[tt]);
+                const float f = __builtin_ldexpf(1.0f, (int)(mref[tt] - m2));
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= f;
+                lsum[tt] *= f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pprev[tt][j] = to_bf16(to_f32(pprev[tt][j]) * f);
+                mref[tt] = m2;
+              }
+            }
+          }
           // P of this chunk and the previous chunk's PV product
           bf16x8 pn[QT];
           probs(qtc, s, mref, pn);

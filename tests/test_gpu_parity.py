@@ -111,21 +111,22 @@ def test_stage_block_attn(orc, dtype, lengths, B):
 
 
 def test_stage_block_attn_large_logits(orc):
-    """Logits far above those of an item's first key chunk.  The bf16 kernel fixes
+    """Logits far above those of an item's first key chunk.  The bf16 kernel sets
     a per-row reference at the first chunk; later scores above it give P an
-    exact power-of-two factor that cancels in O, and the item goes to the
-    exact two-pass fallback only when a row sum or accumulator overflows
-    (about 2^128: a score some 128 doublings or more above the reference,
-    raw score > 128 / log2(e) * sqrt(128) = 1004 here with N(0, 1) values).
-      block 0, head 0: keys 0..31 zero, key 100 and all queries = 7 (score 554,
-                        800 doublings): every row goes to the fallback
+    exact power-of-two factor that cancels in O; a chunk more than 2^32 above
+    the reference raises it (accumulated values scaled by the exact power of
+    two); an item whose row sums or accumulators still overflow goes to the
+    exact two-pass fallback.  Scores in doublings are raw / sqrt(128) * log2(e).
+      block 0, head 0: keys 0..31 zero, key 100 and all queries = 7 (about
+                        800 doublings above the reference): rescaled
       block 0, head 1: keys 0..31 zero, key 195 (partial last chunk) = 7 and
-                        queries = 7: fallback, decided in the masked chunk
-      block 1, head 1: keys 0..31 zero, key 50 and queries = 6 (score 407):
-                        fast path with weights up to 2^52
-      block 2, head 0: keys 0..31 zero, key 50 and queries = 2.47 (about
-                        2^100 above the first chunk's reference, nothing
-                        overflows): fast path
+                        queries = 7: rescaled in the masked chunk
+      block 1, head 1: keys 0..31 zero, key 50 and queries = 6: rescaled
+      block 1, head 0: all keys zero but key 50 = 0.306 and queries = 6
+                        (30 doublings: no rescale, weight 2^30) with every V
+                        = 1e30: the accumulators overflow, so the item takes
+                        the exact fallback
+      block 2, head 0: keys 0..31 zero, key 50 and queries = 2.47: rescaled
     Everything else is N(0, 1)."""
     G.print_case("stage_block_attn_large_logits")
     d, H, B = 256, 2, 200
@@ -144,6 +145,11 @@ def test_stage_block_attn_large_logits(orc):
     qkv[k(slice(200, 232), 1)] = 0.0
     qkv[k(250, 1)] = 6.0
     qkv[q(slice(200, 330), 1)] = 6.0
+    v = lambda r, h: (r, slice(2 * d + h * 128, 2 * d + (h + 1) * 128))
+    qkv[k(slice(200, 330), 0)] = 0.0
+    qkv[k(250, 0)] = 0.306
+    qkv[q(slice(200, 330), 0)] = 6.0
+    qkv[v(slice(200, 330), 0)] = 1e30
     qkv[k(slice(330, 362), 0)] = 0.0
     qkv[k(380, 0)] = 2.47
     qkv[q(slice(330, 420), 0)] = 2.47
