@@ -662,6 +662,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         // cancels in acc / sum, unless something overflows (checked at the end
         // of the item).
         float mref[QT];
+        float sthr[QT];    // raw score above which a row's reference rises
         bf16x8 pprev[QT];  // P of the previous chunk, whose PV product is pending
         int pslot;
         // ---- first key chunk: sets the reference, no PV product yet ----
@@ -676,6 +677,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           for (int tt = 0; tt < QT; ++tt) {
             // the chunk's row max over the 4 lane groups of a query
             mref[tt] = __builtin_ceilf(xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2);
+            sthr[tt] = (mref[tt] + ATT_HEADROOM) / scale_log2;
             lsum[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -695,27 +697,30 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           bf16x8 vf[8];
           read_vt(pslot, vf);
           __builtin_amdgcn_sched_barrier(0);
-          // the chunk's row max (masked keys excluded)
-          float lmax[QT];
-          mask_max(qtc, s, min(ATT_KC, L - kc * ATT_KC), lmax);
+          mask(qtc, s, min(ATT_KC, L - kc * ATT_KC));
           // Lazy rescale: when a row's scores run more than 2^ATT_HEADROOM
           // above its reference, the reference rises to this chunk's
           // ceiling and everything accumulated against the old one (O, the
           // row sum and the pending P) is scaled by the exact power of two
           // between them.  Rare for unit-variance inputs; frequent in deep
           // stacks without normalisation, whose logits grow layer by layer.
+          // The test compares the raw scores with a threshold kept per row.
           {
-            float mnew[QT];
-            bool grow = false;
+            unsigned grow = 0;  // (bitwise: no short-circuit branches)
 #pragma unroll
             for (int tt = 0; tt < QT; ++tt) {
-              mnew[tt] = __builtin_ceilf(xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2);
-              grow = grow || mnew[tt] > mref[tt] + ATT_HEADROOM;
+              const float lm =
+                  fmaxf(fmaxf(fmaxf(s[tt][0][0], s[tt][0][1]), fmaxf(s[tt][0][2], s[tt][0][3])),
+                        fmaxf(fmaxf(s[tt][1][0], s[tt][1][1]), fmaxf(s[tt][1][2], s[tt][1][3])));
+              grow |= (unsigned)(lm > sthr[tt]);
             }
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // (wave-uniform)
+            if (__builtin_amdgcn_ballot_w64(grow != 0) != 0) {  // (wave-uniform, rare)
+              float lmax[QT];
+              mask_max(qtc, s, ATT_KC, lmax);  // (masked keys are -inf already)
 #pragma unroll
               for (int tt = 0; tt < QT; ++tt) {
-                const float m2 = fmaxf(mref[tt], mnew[tt]);
+                const float mnew = __builtin_ceilf(xmax_lanes16(xmax_lanes32(lmax[tt])) * scale_log2);
+                const float m2 = fmaxf(mref[tt], mnew);
                 const float f = __builtin_ldexpf(1.0f, (int)(mref[tt] - m2));
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) oacc[tt][dt] *= f;
@@ -723,6 +728,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
 #pragma unroll
                 for (int j = 0; j < 8; ++j) pprev[tt][j] = to_bf16(to_f32(pprev[tt][j]) * f);
                 mref[tt] = m2;
+                sthr[tt] = (m2 + ATT_HEADROOM) / scale_log2;
               }
             }
           }
