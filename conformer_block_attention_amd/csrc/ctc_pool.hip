@@ -13,8 +13,10 @@
 // class - 1.
 //
 // Kernels:
-//   * position table: one workgroup lists every position (first frame,
-//     frames, sequence) and each sequence's first position, from cu_seqlens;
+//   * position table: one workgroup finds each sequence's first position
+//     (a prefix sum of ceil(len / stride) over cu_seqlens), then one thread
+//     per position finds its sequence by binary search and writes (first
+//     frame, frames, sequence);
 //   * pooled argmax (HBM-bound: it reads the [N][C] logits once): one
 //     workgroup per PA_POS consecutive positions; thread i scores classes
 //     8i + 2048k .. +7 (16-byte loads of bf16 logits) for each of its
@@ -38,9 +40,9 @@ constexpr int PA_MAXWIN = 8;    // frames per pooling window
 // positions the sequences make.  (The table of positions, {first frame,
 // frames, sequence, 0} in order, with frames 0 for entries from that count
 // up to P, is filled by the next kernel.)
-__global__ __launch_bounds__(1024) void build_position_table_kernel(
-    const int* __restrict__ cu, int S, int window, int stride, int P, int4* __restrict__ table,
-    int* __restrict__ pos_cu) {
+__global__ __launch_bounds__(1024) void build_position_table_kernel(const int* __restrict__ cu,
+                                                                   int S, int stride,
+                                                                   int* __restrict__ pos_cu) {
   __shared__ int scan[1024];
   __shared__ int base;
   const int tid = threadIdx.x;
@@ -48,8 +50,7 @@ __global__ __launch_bounds__(1024) void build_position_table_kernel(
   __syncthreads();
   for (int c0 = 0; c0 < S; c0 += 1024) {
     const int s = c0 + tid;
-    const int start = s < S ? cu[s] : 0;
-    const int len = s < S ? cu[s + 1] - start : 0;
+    const int len = s < S ? cu[s + 1] - cu[s] : 0;
     const int n = len > 0 ? (len + stride - 1) / stride : 0;
     scan[tid] = n;
     __syncthreads();
@@ -61,7 +62,6 @@ __global__ __launch_bounds__(1024) void build_position_table_kernel(
     }
     const int first = base + scan[tid] - n;
     if (s < S) pos_cu[s] = first;
-    (void)start;
     __syncthreads();
     if (tid == 1023) base += scan[1023];
     __syncthreads();
@@ -244,8 +244,7 @@ hipError_t launch_bpe_pool_ctc(const void* logits, long long ld, const float* bl
                                hipStream_t stream) {
   int4* table = (int4*)workspace;
   int* pos_cu = (int*)(table + (P > 0 ? P : 1));
-  build_position_table_kernel<<<dim3(1), dim3(1024), 0, stream>>>(cu, S, window, stride, P, table,
-                                                                  pos_cu);
+  build_position_table_kernel<<<dim3(1), dim3(1024), 0, stream>>>(cu, S, stride, pos_cu);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (P > 0) {
