@@ -283,8 +283,8 @@ def bench_ctc(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=workloads.HEADLINE,
                     choices=workloads.WORKLOAD_ORDER + list(workloads.XATTN_WORKLOADS) +
                     [CTC_WORKLOAD])
