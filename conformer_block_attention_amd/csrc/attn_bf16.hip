@@ -305,9 +305,12 @@ __device__ __forceinline__ void swap_row_pairs(unsigned& x, unsigned& y) {
 // last rise; never seen with logits of ordinary size).  Two passes over the keys per query row: the row
 // max, then P with the rounding of the fast path (reference = ceil of the row
 // max in log2 units, P rounded to bf16, the sum taken over the rounded values)
-// and O = sum_j P_j V_j / sum_j P_j, rounded once to bf16.  Waves w0, w0 +
-// nw, ... of the calling waves take one query row each; pbuf holds 64 floats
-// per calling wave.
+// and O = sum_j P_j V_j / sum_j P_j, rounded once to bf16.  Each rounded P is
+// scaled by 2^-ceil(log2 L) before the sums (exact, and it cancels in the
+// ratio): P <= 1 then keeps both sums within the largest |V| and within 1, so
+// V anywhere in the fp32 range cannot overflow them.  Waves w0, w0 + nw, ...
+// of the calling waves take one query row each; pbuf holds 64 floats per
+// calling wave.
 __device__ __forceinline__ float exact_dot(const bf16* __restrict__ a, const bf16* __restrict__ b) {
   float acc = 0.f;
 #pragma unroll 4
@@ -327,6 +330,8 @@ __device__ void exact_item(const bf16* __restrict__ qkv, int4 e, int h, int d, f
   const int row0 = e.x, L = e.y, q0 = e.z, qn = e.w;
   const bf16* kbase = qkv + (size_t)row0 * ld + d + h * DH;
   const bf16* vbase = qkv + (size_t)row0 * ld + 2 * d + h * DH;
+  const int lg = L > 1 ? 32 - __builtin_clz((unsigned)(L - 1)) : 0;  // ceil(log2 L)
+  const float pscale = __builtin_bit_cast(float, (unsigned)(127 - lg) << 23);  // 2^-lg
   for (int i = w0; i < qn; i += nw) {
     const bf16* q = qkv + (size_t)(row0 + q0 + i) * ld + h * DH;
     float mx = -INFINITY;
@@ -339,7 +344,8 @@ __device__ void exact_item(const bf16* __restrict__ qkv, int4 e, int h, int d, f
       float pj = 0.f;
       if (j < L)
         pj = to_f32(to_bf16(__builtin_amdgcn_exp2f(
-            __builtin_fmaf(exact_dot(q, kbase + (size_t)j * ld), scale_log2, -mref))));
+                 __builtin_fmaf(exact_dot(q, kbase + (size_t)j * ld), scale_log2, -mref)))) *
+             pscale;
       psum += pj;
       pbuf[lane] = pj;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -426,7 +432,10 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         copy16_to_lds(vb + c0 + o, dst + (ATT_KC + j * 4) * DH);
       }
     } else {  // the block's partial last chunk: keys past its end repeat its last row
+      // (the chunk's first key goes into the 64-bit base: key * ld can pass
+      // 2^31 in a long block, the distance from k0 cannot)
       const int pc = lane & 15;
+      const size_t c0 = (size_t)k0 * ld * 2;
 #pragma unroll
       for (int j = 0; j < COPIES; ++j) {
         const int r0 = j * 4;
@@ -435,7 +444,8 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
         int key = k0 + kr;
         key = key < c.L ? key : c.L - 1;
         const int lc = pc ^ (isv ? swz_v(kr) : swz_k(kr));
-        copy16_to_lds((isv ? vb : kb) + (unsigned)(key * ld + lc * 8) * 2u, dst + r0 * DH);
+        copy16_to_lds((isv ? vb : kb) + c0 + (unsigned)((key - k0) * ld + lc * 8) * 2u,
+                      dst + r0 * DH);
       }
     }
     ops += COPIES;

@@ -10,9 +10,10 @@
 //
 // Design (one workgroup = 256 threads = 4 waves, one wave per SIMD, one
 // workgroup per CU, persistent):
-//   * output tiles of 256 x BN (BN = 192 for the projection, 128 for
-//     out_proj), waves in a 2 x 2 grid, wave tile 128 x BN/2 of
-//     v_mfma_f32_32x32x16_bf16 with fp32 accumulators in AGPRs.
+//   * output tiles of BM x BN (256 x 192 for the projection, 256 x 128 for
+//     out_proj; 64..256 x 128 for one round of small tiles after the
+//     two-wave kernel's whole rounds), waves in a 2 x 2 grid, wave tile
+//     BM/2 x BN/2 of v_mfma_f32_32x32x16_bf16 with fp32 accumulators in AGPRs.
 //   * one flat stream of K steps (of BK = 32) over all of the workgroup's tiles
 //     flows through an NST-stage LDS ring filled by 16-byte global->LDS
 //     direct copies.  The copies run NST-1 steps ahead of the math and cross
@@ -28,13 +29,16 @@
 //   * out_proj: the residual is prefetched a few steps before the end of the
 //     tile in the same 16-byte-piece layout and added in fp32 before the one
 //     RNE rounding.
-//   * tile order: the 8 XCDs receive workgroup ids round-robin; each XCD
-//     owns a contiguous range of 256-row panels and walks them in groups of
-//     8 panels, panel fastest, so the 32 tiles one XCD runs at a time share
-//     8 activation panels and 4 weight slices in its L2.
-//   * rows >= M are read as row M-1, so their results equal row M-1's bit for
-//     bit; stores need no mask (a duplicate row writes the same bits).
-//     Requires K % BK == 0 and Nc % BN == 0.
+//   * tile order (more tiles than workgroups): the 8 XCDs receive workgroup
+//     ids round-robin; each XCD owns a contiguous range of BM-row panels and
+//     walks them in groups of 8 panels, panel fastest, so the 32 tiles one
+//     XCD runs at a time share 8 activation panels and 4 weight slices in its
+//     L2.  With at most one tile per workgroup, tile = workgroup id.
+//   * rows >= M of A are read as row M-1; their results are never stored.
+//     The output and the residual go through buffer resources that end at
+//     row M of the tile, so the hardware drops the stores of rows >= M and
+//     their residual reads return zero (a stored copy of row M-1 would race
+//     with C == R in place).  Requires K % BK == 0 and Nc % BN == 0.
 #include "gs_device.hpp"
 
 namespace gs {
@@ -136,18 +140,20 @@ __device__ __forceinline__ void swap_lo_hi(unsigned& x, unsigned& y) {
   y = s[1];
 }
 
-template <int BN, int BK, int NST, bool DEFER, int EARLY, int SPLIT, bool RESID>
+template <int BM, int BN, int BK, int NST, bool DEFER, int EARLY, int SPLIT, bool RESID>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* R, bf16* C,
     int M, int Nc, int K) {
   using G = TileGeom<BK>;
-  using CopyA = TileCopy<GEMM_BM, BK, true>;   // activation rows: the last panel is ragged
+  using CopyA = TileCopy<BM, BK, true>;        // activation rows: the last panel is ragged
   using CopyB = TileCopy<BN, BK, false>;       // weight rows: Nc % BN == 0
+  constexpr int WM = BM / 2;   // wave tile rows
   constexpr int WN = BN / 2;   // wave tile columns
-  constexpr int TI = 4;        // 32-row MFMA tiles per wave (128 rows)
+  constexpr int TI = WM / 32;  // 32-row MFMA tiles per wave
   constexpr int TJ = WN / 32;  // 32-col MFMA tiles per wave
   constexpr int KK = BK / 16;  // MFMA k chunks per K step
-  constexpr int A_ELEMS = GEMM_BM * BK, B_ELEMS = BN * BK;
+  constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
+  static_assert(BM % 64 == 0 && BM <= 256, "row tile");
   constexpr int STAGE = A_ELEMS + B_ELEMS;
   constexpr int LPS = CopyA::INSTR + CopyB::INSTR;  // copies per step per wave
   constexpr int NOUT = TI * TJ * 2;                 // 16-byte output pieces per lane per tile
@@ -164,14 +170,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   const int frag_row = lane & 31;
   const int half = lane >> 5;
 
-  const int mt_count = (M + GEMM_BM - 1) / GEMM_BM;
+  const int mt_count = (M + BM - 1) / BM;
   const int nt_count = Nc / BN;
   const int KT = K / BK;
 
   // ---- tile order ----
   // k-th tile of this workgroup as (panel, column tile), or panel = -1.
   const int Gs = gridDim.x;
-  const bool by_xcd = (Gs & 7) == 0 && mt_count >= 8;  // else: plain round-robin over tiles
+  // (else: plain round-robin over tiles)
+  const bool by_xcd = (Gs & 7) == 0 && mt_count >= 8 && (long long)mt_count * nt_count > Gs;
   const int xcd = blockIdx.x & 7;
   const int p_lo = by_xcd ? (int)(((long long)xcd * mt_count) >> 3) : 0;
   const int p_hi = by_xcd ? (int)(((long long)(xcd + 1) * mt_count) >> 3) : mt_count;
@@ -211,9 +218,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   const bf16* tA = nullptr;
   const bf16* tB = nullptr;
   auto set_issue_tile = [&]() __attribute__((always_inline)) {
-    tA = A + (size_t)is_panel * GEMM_BM * K;
+    tA = A + (size_t)is_panel * BM * K;
     tB = W + (size_t)is_col * BN * K;
-    cpA.init(is_panel * GEMM_BM, M, K, wave, lane);
+    cpA.init(is_panel * BM, M, K, wave, lane);
     cpB.init(is_col * BN, Nc, K, wave, lane);
   };
   set_issue_tile();
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   static_assert((32 / G::RPW) % G::CPR == 0, "swizzle must repeat every 32 rows");
   auto load_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
     const int lo = frag_row * BK + ((kk * 2 + half) ^ G::swz(frag_row)) * 8;
-    const GS_LDS bf16* as = stage_a(st) + wm * 128 * BK + lo;
+    const GS_LDS bf16* as = stage_a(st) + wm * WM * BK + lo;
     const GS_LDS bf16* bs = stage_b(st) + wn * WN * BK + lo;
 #pragma unroll
     for (int i = 0; i < TI; ++i) af[i] = *(const GS_LDS bf16x8*)(as + i * 32 * BK);
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   };
 
   // ---- output pieces ----
-  // Piece q = (i*TJ + j)*2 + gp of a lane: row wm*128 + i*32 + lane%32 of the
+  // Piece q = (i*TJ + j)*2 + gp of a lane: row wm*WM + i*32 + lane%32 of the
   // tile, columns wn*WN + j*32 + (2*gp + lane/32)*8 .. +7.  Its byte offset
   // from the tile's origin is row_off[i] + a column constant.  Pieces below
   // EARLY are stored as soon as they are formed; vals[q - EARLY] holds the
@@ -262,20 +269,23 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   u32x4_t vals[NOUT > EARLY ? NOUT - EARLY : 1];
   u32x4_t rres[RESID ? NOUT : 1];
   unsigned row_off[TI];        // for the tile whose pieces vals holds
-  char* out_base = nullptr;    // C at that tile's origin (uniform)
+  __amdgpu_buffer_rsrc_t out_rs = buffer_rsrc(C, 0);  // that tile's rows below M
   bool have_out = false;
   int mark_r = 0;
   auto piece_col_bytes = [&](int q) { return ((q / 2 % TJ) * 32 + (q % 2) * 16) * 2; };
-  auto tile_row_offsets = [&](int m0, unsigned* ro) __attribute__((always_inline)) {
+  // offsets of a lane's rows from the tile's origin (rows >= M included)
+  auto tile_row_offsets = [&](unsigned* ro) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      int m = m0 + wm * 128 + i * 32 + frag_row;
-      m = m < M ? m : M - 1;
-      ro[i] = (unsigned)((m - m0) * Nc + wn * WN + half * 8) * 2u;
-    }
+    for (int i = 0; i < TI; ++i)
+      ro[i] = (unsigned)((wm * WM + i * 32 + frag_row) * Nc + wn * WN + half * 8) * 2u;
+  };
+  // bytes from the tile's origin (m0, n0) to the end of its last row below M
+  auto tile_bytes = [&](int m0, int n0) __attribute__((always_inline)) {
+    return (unsigned)(min(M - m0, BM) * Nc - n0) * 2u;
   };
   auto store_piece = [&](int q) __attribute__((always_inline)) {
-    *(u32x4_t*)(out_base + row_off[q / (2 * TJ)] + piece_col_bytes(q)) = vals[q - EARLY];
+    __builtin_amdgcn_raw_buffer_store_b128(vals[q - EARLY], out_rs,
+                                           row_off[q / (2 * TJ)] + piece_col_bytes(q), 0, 0);
   };
   auto store_pieces = [&](int q0, int nq) __attribute__((always_inline)) {
 #pragma unroll
@@ -285,10 +295,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   auto load_residual = [&](int m0, int n0) __attribute__((always_inline)) {
     if constexpr (RESID) {
       unsigned ro[TI];
-      tile_row_offsets(m0, ro);
-      const char* rb = (const char*)(R + (size_t)m0 * Nc + n0);
+      tile_row_offsets(ro);
+      const auto res_rs = buffer_rsrc(R + (size_t)m0 * Nc + n0, tile_bytes(m0, n0));
 #pragma unroll
-      for (int q = 0; q < NOUT; ++q) rres[q] = *(const u32x4_t*)(rb + ro[q / (2 * TJ)] + piece_col_bytes(q));
+      for (int q = 0; q < NOUT; ++q)
+        rres[q] = __builtin_amdgcn_raw_buffer_load_b128(res_rs, ro[q / (2 * TJ)] + piece_col_bytes(q),
+                                                        0, 0);
       ops += NOUT;
       mark_r = ops;
     }
@@ -313,7 +325,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
 
   f32x16 acc[TI][TJ];
   for (;;) {
-    const int m0 = panel * GEMM_BM, n0 = col * BN;
+    const int m0 = __builtin_amdgcn_readfirstlane(panel * BM);
+    const int n0 = __builtin_amdgcn_readfirstlane(col * BN);
     const int rstep = KT > RPRE ? KT - RPRE : 0;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
         }
         const int nkk = last ? 0 : kk + 1;
         const int lo = frag_row * BK + ((nkk * 2 + half) ^ G::swz(frag_row)) * 8;
-        const GS_LDS bf16* as = stage_a(nslot) + wm * 128 * BK + lo;
+        const GS_LDS bf16* as = stage_a(nslot) + wm * WM * BK + lo;
         const GS_LDS bf16* bs = stage_b(nslot) + wn * WN * BK + lo;
         // side instructions of this chunk: fragment reads, copies c0..c1-1,
         // output pieces s0..s1-1
@@ -411,8 +424,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
     // and 2gp+1, the swap leaves lane l (< 32) with all 8 columns of group
     // 2gp and lane l+32 with all 8 of group 2gp+1.
     if constexpr (RESID) gemm_wait_vmcnt_le(__builtin_amdgcn_readfirstlane(ops - mark_r));
-    tile_row_offsets(m0, row_off);
-    out_base = (char*)(C + (size_t)m0 * Nc + n0);
+    tile_row_offsets(row_off);
+    out_rs = buffer_rsrc(C + (size_t)m0 * Nc + n0, tile_bytes(m0, n0));
     have_out = true;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -458,7 +471,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
             piece = u32x4_t{x0, x1, y0, y1};
           }
           if (q < EARLY) {
-            *(u32x4_t*)(out_base + row_off[i] + piece_col_bytes(q)) = piece;
+            __builtin_amdgcn_raw_buffer_store_b128(piece, out_rs, row_off[i] + piece_col_bytes(q),
+                                                   0, 0);
             ++ops;
           } else {
             vals[q - EARLY] = piece;
@@ -501,7 +515,7 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int 
   if ((3 * d) % 256 == 0) return launch_qkv_proj_bf16_pp(x, wqkv, qkv, M, d, stream);
   const int Nc = 3 * d;
   const int mt = (M + GEMM_BM - 1) / GEMM_BM;
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<192, 64, 2, false, 0, 12, false>), dim3(gemm_persistent_grid(mt * (Nc / 192))),
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<GEMM_BM, 192, 64, 2, false, 0, 12, false>), dim3(gemm_persistent_grid(mt * (Nc / 192))),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)x, (const bf16*)wqkv,
                      (const bf16*)nullptr, (bf16*)qkv, M, Nc, d);
   return hipGetLastError();
@@ -514,9 +528,50 @@ hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, vo
                                 int d, hipStream_t stream) {
   if (d % 256 == 0) return launch_out_proj_bf16_pp(o, wo, x, out, M, d, stream);
   const int mt = (M + GEMM_BM - 1) / GEMM_BM;
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<128, 64, 3, false, 0, 8, true>), dim3(gemm_persistent_grid(mt * (d / 128))),
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<GEMM_BM, 128, 64, 3, false, 0, 8, true>), dim3(gemm_persistent_grid(mt * (d / 128))),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)o, (const bf16*)wo,
                      (const bf16*)x, (bf16*)out, M, d, d);
+  return hipGetLastError();
+}
+
+// One round of small tiles: C[rows][Nc] (+ R) for the rows left after a
+// persistent launch's whole rounds of large tiles.  Tiles are BM x 128 with
+// BM the smallest of 64, 128, 192, 256 whose tiles all fit on the CUs at
+// once, so every CU takes at most one small tile instead of a few CUs taking
+// a whole round of large ones.  Returns that BM, or 0 if even 256-row tiles
+// would need a second round (the caller then keeps one launch).
+int gemm_tail_tile_rows(int rows, int Nc) {
+  const int cus = gemm_persistent_grid(1 << 30);
+  if (rows <= 0 || Nc % 128 != 0) return 0;
+  for (int bm = 64; bm <= 256; bm += 64)
+    if ((long long)((rows + bm - 1) / bm) * (Nc / 128) <= cus) return bm;
+  return 0;
+}
+
+template <int BM, bool RESID>
+static void launch_tail(const bf16* A, const bf16* W, const bf16* R, bf16* C, int rows, int Nc,
+                        int K, hipStream_t stream) {
+  const int tiles = (rows + BM - 1) / BM * (Nc / 128);
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, 128, 64, 3, false, 0, 4, RESID>), dim3(tiles),
+                     dim3(GEMM_THREADS), 0, stream, A, W, R, C, rows, Nc, K);
+}
+
+// bm: gemm_tail_tile_rows(rows, Nc); requires K % 64 == 0.
+hipError_t launch_gemm_tail_bf16(const void* A, const void* W, const void* R, void* C, int rows,
+                                 int Nc, int K, int bm, hipStream_t stream) {
+  const bf16 *a = (const bf16*)A, *w = (const bf16*)W, *r = (const bf16*)R;
+  bf16* c = (bf16*)C;
+  switch (bm * 2 + (R != nullptr)) {
+    case 128: launch_tail<64, false>(a, w, r, c, rows, Nc, K, stream); break;
+    case 129: launch_tail<64, true>(a, w, r, c, rows, Nc, K, stream); break;
+    case 256: launch_tail<128, false>(a, w, r, c, rows, Nc, K, stream); break;
+    case 257: launch_tail<128, true>(a, w, r, c, rows, Nc, K, stream); break;
+    case 384: launch_tail<192, false>(a, w, r, c, rows, Nc, K, stream); break;
+    case 385: launch_tail<192, true>(a, w, r, c, rows, Nc, K, stream); break;
+    case 512: launch_tail<256, false>(a, w, r, c, rows, Nc, K, stream); break;
+    case 513: launch_tail<256, true>(a, w, r, c, rows, Nc, K, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -34,8 +34,12 @@
 //     range, so its share differs from the others' by at most one tile) and
 //     its workgroups take its tiles in turn, so the tiles one XCD runs at a
 //     time share a few activation panels and weight slices in its L2.
-//   * rows >= M are read as row M-1, so their results equal row M-1's bit for
-//     bit; stores need no mask (a duplicate row writes the same bits).
+//   * rows >= M of A are read as row M-1; their results are never stored.
+//     The output and the residual go through buffer resources that end at
+//     row M of the tile, so the hardware drops the stores of rows >= M and
+//     their residual reads return zero.  (Letting such a row store a copy of
+//     row M-1 would race with C == R in place: another wave may already have
+//     written row M-1 when the copy reads its residual.)
 //     Requires K % 64 == 0 and Nc % BN == 0.
 #include "gs_device.hpp"
 
@@ -281,23 +285,25 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
   // l+32 with all 8 of group 2gp+1: piece (i, j, gp) of a lane is row
   // wm*128 + i*32 + lane%32, columns wn*WN + j*32 + gp*16 + (lane/32)*8 .. +7.
   auto store_tile = [&](int m0, int n0) __attribute__((always_inline)) {
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
     unsigned ro[TI];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      int m = m0 + wm * 128 + i * 32 + frag_row;
-      m = m < M ? m : M - 1;
-      ro[i] = (unsigned)((m - m0) * Nc + wn * WN + half * 8) * 2u;
-    }
-    char* ob = (char*)(C + (size_t)m0 * Nc + n0);
+    for (int i = 0; i < TI; ++i)
+      ro[i] = (unsigned)((wm * 128 + i * 32 + frag_row) * Nc + wn * WN + half * 8) * 2u;
+    // bytes from the tile's origin to the end of its last row below M
+    const unsigned tile_bytes = (unsigned)(min(M - m0, BM) * Nc - n0) * 2u;
+    const auto out_rs = buffer_rsrc(C + (size_t)m0 * Nc + n0, tile_bytes);
     // the residual pieces, all loaded first (the fragments are dead here)
     u32x4_t rres[RESID ? TI * TJ * 2 : 1];
     if constexpr (RESID) {
-      const char* rb = (const char*)(R + (size_t)m0 * Nc + n0);
+      const auto res_rs = buffer_rsrc(R + (size_t)m0 * Nc + n0, tile_bytes);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int q = 0; q < TJ * 2; ++q)
-          rres[i * TJ * 2 + q] = *(const u32x4_t*)(rb + ro[i] + ((q >> 1) * 32 + (q & 1) * 16) * 2);
+          rres[i * TJ * 2 + q] = __builtin_amdgcn_raw_buffer_load_b128(
+              res_rs, ro[i] + ((q >> 1) * 32 + (q & 1) * 16) * 2, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
@@ -338,7 +344,8 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
             swap_lo_hi(x1, y1);
             piece = u32x4_t{x0, x1, y0, y1};
           }
-          *(u32x4_t*)(ob + ro[i] + (j * 32 + gp * 16) * 2) = piece;
+          __builtin_amdgcn_raw_buffer_store_b128(piece, out_rs, ro[i] + (j * 32 + gp * 16) * 2,
+                                                 0, 0);
         }
     }
     ops += NOUT + (RESID ? NOUT : 0);
@@ -416,56 +423,59 @@ static int pp_persistent_grid(int tiles) {
   return tiles < g_pp_cus ? tiles : g_pp_cus;
 }
 
-// Load balance: when the 256 x 256 tiles leave a partial last round and the
-// panels (256-row strips) that fill the whole rounds fill them exactly, those
-// panels run first and the remaining ones follow as a second launch of
-// 256 x 128 tiles, provided these fit one round.  Returns the first row of
-// the second part (M when one launch is kept).  For M = 55093 on 256 CUs,
-// out_proj (4 tiles per panel) runs 192 panels in 3 rounds and 24 panels as
-// 192 half tiles instead of 4 rounds for 3.4 rounds of work.  qkv_proj
-// (12 tiles per panel) keeps one launch: its 10.1 rounds leave a last round
-// of 32 tiles, which run faster than a full round (less contention for L2
-// and memory), and a split there (213 panels, then 3 as half tiles) measured
-// no faster.
-static int pp_split_rows(int M, int tiles_per_panel) {
+int gemm_tail_tile_rows(int rows, int Nc);
+hipError_t launch_gemm_tail_bf16(const void* A, const void* W, const void* R, void* C, int rows,
+                                 int Nc, int K, int bm, hipStream_t stream);
+
+// Load balance: 256 x 256 tiles over the CUs leave a partial last round,
+// which a few CUs would run while the others wait.  The panels (256-row
+// strips) that fill whole rounds run as the persistent launch; the rows
+// after them run as a second launch of one round of small tiles (BM x 128,
+// BM chosen so that every tile has a CU of its own), if such a round can
+// hold them.  Returns the first row of that second part (M when one launch
+// is kept) and its row tile in *tail_bm.  For M = 55093 on 256 CUs: the
+// projection (12 tiles per panel) runs 213 panels in 10 rounds, then 565
+// rows as 216 tiles of 64 x 128; out_proj (4 tiles per panel) runs 192
+// panels in 3 rounds, then 6144 rows as 256 tiles of 192 x 128.
+static int pp_split_rows(int M, int Nc, int* tail_bm) {
+  const int tiles_per_panel = Nc / 256;
   const int mt = (M + pp::BM - 1) / pp::BM;
   const int cus = pp_persistent_grid(1 << 30);
   const long long tiles = (long long)mt * tiles_per_panel;
-  const int rounds = (int)(tiles / cus);
-  if (rounds < 1 || ((long long)rounds * cus) % tiles_per_panel != 0) return M;
-  const int main_panels = (int)((long long)rounds * cus / tiles_per_panel);
-  const int rest = mt - main_panels;
-  if (rest <= 0 || rest * 2 * tiles_per_panel > cus) return M;
+  const long long rounds = tiles / cus;
+  *tail_bm = 0;
+  if (rounds < 1 || tiles % cus == 0) return M;
+  const int main_panels = (int)(rounds * cus / tiles_per_panel);
+  const int rest = M - main_panels * pp::BM;
+  if (rest <= 0) return M;
+  const int bm = gemm_tail_tile_rows(rest, Nc);
+  if (bm == 0) return M;
+  *tail_bm = bm;
   return main_panels * pp::BM;
-}
-
-// C[r0 .. r0+rows) for one part of the row split (RESID: out_proj).
-template <int BN, bool RESID>
-static void pp_launch_part(const bf16* A, const bf16* W, const bf16* R, bf16* C, int r0, int rows,
-                           int Nc, int K, hipStream_t stream, const int* m_dev = nullptr) {
-  const int mt = (rows + pp::BM - 1) / pp::BM;
-  const size_t a_off = (size_t)r0 * K, c_off = (size_t)r0 * Nc;
-  hipLaunchKernelGGL((gemm_pp_bf16_kernel<BN, RESID, 2>), dim3(pp_persistent_grid(mt * (Nc / BN))),
-                     dim3(pp::THREADS), 0, stream, A + a_off, W, RESID ? R + c_off : R, C + c_off,
-                     rows, Nc, K, m_dev);
 }
 
 // m_dev (optional): the row count on the device, at most M; one launch then.
 template <bool RESID>
 static hipError_t pp_launch(const bf16* A, const bf16* W, const bf16* R, bf16* C, int M, int Nc,
                             int K, hipStream_t stream, const int* m_dev = nullptr) {
+  auto launch = [&](int rows, const int* md) {
+    const int mt = (rows + pp::BM - 1) / pp::BM;
+    hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, RESID, 2>),
+                       dim3(pp_persistent_grid(mt * (Nc / 256))), dim3(pp::THREADS), 0, stream, A,
+                       W, R, C, rows, Nc, K, md);
+  };
   if (m_dev) {
-    pp_launch_part<256, RESID>(A, W, R, C, 0, M, Nc, K, stream, m_dev);
+    launch(M, m_dev);
     return hipGetLastError();
   }
-  const int m1 = pp_split_rows(M, Nc / 256);
-  pp_launch_part<256, RESID>(A, W, R, C, 0, m1, Nc, K, stream);
-  if (m1 < M) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    pp_launch_part<128, RESID>(A, W, R, C, m1, M - m1, Nc, K, stream);
-  }
-  return hipGetLastError();
+  int tail_bm = 0;
+  const int m1 = pp_split_rows(M, Nc, &tail_bm);
+  launch(m1, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || m1 == M) return e;
+  const size_t a_off = (size_t)m1 * K, c_off = (size_t)m1 * Nc;
+  return launch_gemm_tail_bf16(A + a_off, W, RESID ? R + c_off : nullptr, C + c_off, M - m1, Nc,
+                               K, tail_bm, stream);
 }
 
 hipError_t launch_qkv_proj_bf16_pp(const void* x, const void* wqkv, void* qkv, int M, int d,

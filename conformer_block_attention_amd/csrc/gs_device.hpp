@@ -40,4 +40,14 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Raw buffer resource over [base, base + bytes) (stride 0; gfx9 word 3).
+// Accesses through it are range-checked by the hardware: a load past the end
+// returns zero and a store past the end is dropped, while the instruction
+// still issues for the whole wave (so it counts in vmcnt like any other).
+// base and bytes must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 }  // namespace gs

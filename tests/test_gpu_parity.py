@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from conformer_block_attention_amd import gsattn, workloads
+from conformer_block_attention_amd import accounting, gsattn, workloads
 from tests import gpu_common as G
 
 pytestmark = pytest.mark.gpu
@@ -58,6 +58,27 @@ def test_stage_qkv_proj(orc, dtype):
     worst = float(np.max(np.abs(got - ref) / bound))
     print(f"  worst error / bound = {worst:.3f}", flush=True)
     assert worst <= 1.0, worst
+
+
+def test_stage_qkv_proj_tail_launch(orc):
+    """17000 rows, d = 1024: 804 tiles of 256 x 256 for 256 CUs.  The bf16
+    path runs the first 64 panels in 3 whole rounds and the last 616 rows as
+    one round of 64 x 128 tiles (240 of them); every element against the
+    a-priori bound, rows of both launches reported."""
+    G.print_case("stage_qkv_proj_tail_launch")
+    n = 17000
+    case = workloads.custom_case([n], 1024, 8, 200, torch.bfloat16, seed=8)
+    x, _, wqkv, _ = G.on_dev(case)
+    qkv = gsattn.qkv_proj(x, wqkv)
+    torch.cuda.synchronize()
+    ref = orc.qkv_proj(case.x, case.weights[0][0])
+    got = qkv.double().cpu().numpy()
+    bound = _gemm_bound(case.x.double().numpy(), case.weights[0][0].double().numpy(), ref,
+                        torch.bfloat16)
+    r = np.abs(got - ref) / bound
+    print(f"  worst error / bound = {float(r.max()):.3f} (rows past 16384: "
+          f"{float(r[64 * 256:].max()):.3f})", flush=True)
+    assert float(r.max()) <= 1.0
 
 
 def _attn_bound(qkv, cu, heads, B, o_ref, dtype):
@@ -166,6 +187,75 @@ def test_stage_block_attn_large_logits(orc):
     assert worst <= 1.0, worst
 
 
+def test_stage_block_attn_many_overflowed_items(orc):
+    """More overflowed items per workgroup than its list of flagged items
+    holds (64), so the exact recompute scans every item's flag word; and
+    values near the top of the fp32 range in the recompute itself.
+
+    Blocks of 64 rows (two key chunks), d = 512, 4 heads, 420 000 rows:
+      head 0: near-equal scores and V in [2.5e37, 3.5e37]: even with P <= 1
+              the sums of 32 or 64 keys pass the fp32 range unless scaled;
+      heads 1, 2: queries 6, keys 0 but row 50 of each block 0.306 (30
+              doublings above the first chunk's reference, so no rise),
+              V in [0.5e30, 1.5e30]: the accumulators overflow;
+      head 3: N(0, 1), never flagged.
+    Items are dealt round-robin in snake order to 256 workgroups and an item's
+    head is its index mod 4, so workgroup w sees only heads w mod 4 and
+    3 - w mod 4: about 100 flagged items (the scan) where those are 1 and 2,
+    about 50 (the list) where they are 0 and 3."""
+    d, H, B = 512, 4, 64
+    lengths = [419000, 1000]
+    n = sum(lengths)
+    G.print_case("stage_block_attn_many_overflowed_items", n=n, B=B, H=H)
+    g = torch.Generator().manual_seed(17)
+    qkv = torch.zeros(n, 3 * d)
+    hq = lambda h: slice(h * 128, (h + 1) * 128)
+    hk = lambda h: slice(d + h * 128, d + (h + 1) * 128)
+    hv = lambda h: slice(2 * d + h * 128, 2 * d + (h + 1) * 128)
+    qkv[:, hq(0)] = 0.05 * torch.randn(n, 128, generator=g)
+    qkv[:, hk(0)] = 0.05 * torch.randn(n, 128, generator=g)
+    qkv[:, hv(0)] = 1e37 * (3.0 + torch.rand(n, 128, generator=g) - 0.5)
+    rel = torch.arange(n) - torch.from_numpy(np.repeat(workloads.cu_seqlens(lengths)[:-1],
+                                                       lengths).astype(np.int64))
+    jump = (rel % B) == 50
+    for h in (1, 2):
+        qkv[:, hq(h)] = 6.0
+        qkv[jump, hk(h)] = 0.306
+        qkv[:, hv(h)] = 1e30 * (1.0 + torch.rand(n, 128, generator=g) - 0.5)
+    qkv[:, hq(3)] = torch.randn(n, 128, generator=g)
+    qkv[:, hk(3)] = torch.randn(n, 128, generator=g)
+    qkv[:, hv(3)] = torch.randn(n, 128, generator=g)
+    qkv_cpu = qkv.to(torch.bfloat16)
+    del qkv
+    cu = workloads.cu_seqlens(lengths)
+    items = sum((l + B - 1) // B for l in lengths) * H
+    # about items / 256 per workgroup: all flagged where the heads are 1 and 2,
+    # half where they are 0 and 3
+    assert 65 * 256 < items < 2 * 64 * 256
+    o = gsattn.block_attn(qkv_cpu.to(G.dev()), torch.from_numpy(cu).to(G.dev()), H, B)
+    torch.cuda.synchronize()
+    got = o.double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    ref = orc.block_attn(qkv_cpu, cu, H, B)
+    for h in range(3):
+        # every item recomputed: the rounding of P to bf16 and of O only
+        err = G.rel_err(got[:, h * 128:(h + 1) * 128], ref[:, h * 128:(h + 1) * 128])
+        print(f"  items={items} head {h}: err={err:.3e}", flush=True)
+        assert err <= G.BF16_TOL, (h, err)
+    # head 3 (ordinary values, the fast path), element by element against the
+    # a-priori bound on the first 100 blocks and the second sequence
+    rows = np.r_[0:100 * B, n - 1000:n]
+    sub_cu = np.array([0, 100 * B, 100 * B + 1000], np.int32)
+    sub = qkv_cpu[torch.from_numpy(rows)]
+    ref_s = orc.block_attn(sub, sub_cu, H, B)
+    assert np.array_equal(ref_s, ref[rows])  # blocks are independent
+    bound = _attn_bound(sub.double().numpy(), sub_cu, H, B, ref_s, torch.bfloat16)
+    c = slice(3 * 128, 4 * 128)
+    worst = float(np.max(np.abs(got[rows][:, c] - ref_s[:, c]) / bound[:, c]))
+    print(f"  head 3: worst error / bound = {worst:.3f}", flush=True)
+    assert worst <= 1.0, worst
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_stage_out_proj(orc, dtype):
     G.print_case("stage_out_proj", dtype=dtype)
@@ -186,8 +276,9 @@ def test_stage_out_proj(orc, dtype):
 
 def test_stage_out_proj_tail_launch(orc):
     """17000 rows, d = 1024: 67 panels of 256 rows, more 256 x 256 tiles than CUs.
-    The bf16 path runs the first 64 panels in whole rounds and the last 3 as a
-    second launch of 256 x 128 tiles; both parts are checked."""
+    The bf16 path runs the first 64 panels in one whole round and the last 616
+    rows as a second launch of one round of 64 x 128 tiles; both parts are
+    checked."""
     G.print_case("stage_out_proj_tail_launch")
     n = 17000
     case = workloads.custom_case([n], 1024, 8, 200, torch.bfloat16, seed=4)
@@ -220,21 +311,26 @@ def test_workload_bf16_t800(orc):
 
 
 @pytest.mark.parametrize("name", ["bf16_b32_long", "bf16_b128_lognormal"])
-def test_workload_full_size_sampled(orc, name):
-    """Full size, launch configuration of the benchmark; oracle on sampled blocks."""
+def test_workload_full_size(orc, name):
+    """Full size, in the benchmark's launch configuration: every row against
+    the oracle; run-to-run bit equality; a few sequences run alone give the
+    bits they get packed."""
     G.print_case(name)
     case = workloads.build_case(workloads.WORKLOADS[name])
     x, cu, wqkv, wo = G.on_dev(case)
     out = G.run(x, cu, wqkv, wo, case.block_frames, case.heads)
     out2 = G.run(x, cu, wqkv, wo, case.block_frames, case.heads)
     assert torch.equal(out, out2), "run-to-run results differ"
-    mask = G.sample_mask(case.lengths, case.block_frames, n_random=6, seed=1)
     ref = orc.block_mhsa(case.x, case.cu, case.weights[0][0], case.weights[0][1],
-                         case.block_frames, case.heads, mask=mask)
-    sel = mask.astype(bool)
-    got = out.double().cpu().numpy()[sel]
-    err = G.rel_err(got, ref[sel])
-    print(f"  sampled rows={int(sel.sum())} err={err:.3e}", flush=True)
+                         case.block_frames, case.heads)
+    got = out.double().cpu().numpy()
+    err = G.rel_err(got, ref)
+    # per block, to name the worst one
+    bt = accounting.block_table(case.lengths, case.block_frames)
+    worst = max(range(len(bt)), key=lambda i: float(np.max(np.abs(
+        got[bt[i][0]:bt[i][0] + bt[i][1]] - ref[bt[i][0]:bt[i][0] + bt[i][1]]))))
+    print(f"  rows={case.n_frames} blocks={len(bt)} err={err:.3e} (worst block {worst} at row "
+          f"{bt[worst][0]}, length {bt[worst][1]})", flush=True)
     assert err <= G.BF16_TOL, err
     # packing invariance on a few sequences: packed rows == that sequence run alone (bitwise)
     for s in (0, len(case.lengths) // 2, len(case.lengths) - 1):
@@ -244,14 +340,15 @@ def test_workload_full_size_sampled(orc, name):
         assert torch.equal(one, out[a:b]), f"sequence {s} differs when run alone"
 
 
-def test_full_sequence_attention_sampled(orc):
+def test_full_sequence_attention_boundaries(orc):
     """One block per sequence (block length above every length): full
     bidirectional attention over each packed sequence of the long-clip batch,
     32 sequences of 1950..4700 frames, in the launch configuration of the
-    benchmark.  The oracle computes sampled query rows of three sequences:
-    both ends, both sides of every 224-row query-group boundary, random rows.
-    The same call with a larger block length gives the same bits, and a
-    sequence run alone gives the bits it gets packed."""
+    benchmark.  The oracle computes sampled query rows of every sequence:
+    both ends and both sides of every 224-row query-group boundary, plus 32
+    random rows each of three sequences.  The same call with a larger block
+    length gives the same bits, and a sequence run alone gives the bits it
+    gets packed."""
     name = "bf16_b32_long_full"
     case = workloads.build_case(workloads.WORKLOADS[name])
     G.print_case(name, frames=case.n_frames, block_frames=case.block_frames)
@@ -261,12 +358,13 @@ def test_full_sequence_attention_sampled(orc):
     rng = np.random.default_rng(3)
     mask = np.zeros(case.n_frames, np.uint8)
     seqs = (0, len(case.lengths) // 2, len(case.lengths) - 1)
-    for s in seqs:
+    for s in range(len(case.lengths)):
         a, L = int(case.cu[s]), int(case.lengths[s])
         rows = {0, 1, L - 2, L - 1}
         for g in range(224, L, 224):
             rows.update((g - 1, g))
-        rows.update(int(r) for r in rng.choice(L, size=32, replace=False))
+        if s in seqs:
+            rows.update(int(r) for r in rng.choice(L, size=32, replace=False))
         mask[[a + r for r in rows]] = 1
     ref = orc.block_mhsa(case.x, case.cu, case.weights[0][0], case.weights[0][1],
                          case.block_frames, case.heads, mask=mask)
@@ -363,9 +461,9 @@ def test_padded_lengths_outside_the_bucket_are_clamped():
     assert torch.equal(out, out_ref) and torch.equal(out_big, out_ref)
 
 
-def test_padded_bucket_workload_sampled(orc):
+def test_padded_bucket_workload(orc):
     """128 buckets of 800 rows holding the headline batch's lengths capped at
-    800, as the benchmark runs them: sampled buckets against the oracle,
+    800, as the benchmark runs them: every valid row against the oracle,
     padding rows equal to x everywhere, valid rows bit for bit those of the
     packed entry point on the same sequences."""
     name = "bf16_bucket800_b128"
@@ -382,17 +480,12 @@ def test_padded_bucket_workload_sampled(orc):
     s = len(case.lengths)
     rows = np.arange(s * t)
     valid = (rows % t) < np.repeat(case.lengths, t)
-    pick = sorted({0, s // 2, s - 1, int(np.argmax(case.lengths)), int(np.argmin(case.lengths))})
-    mask = np.zeros(s * t, np.uint8)
-    for b in pick:
-        mask[b * t:(b + 1) * t] = 1
-    mask &= valid.astype(np.uint8)
     ref = orc.block_mhsa_padded(case.x, case.lengths, t, case.weights[0][0], case.weights[0][1],
-                                case.block_frames, case.heads, mask=mask)
-    sel = mask.astype(bool)
+                                case.block_frames, case.heads)
+    sel = valid
     flat = out.reshape(-1, d)
     err = G.rel_err(flat.double().cpu().numpy()[sel], ref[sel])
-    print(f"  buckets={pick} sampled rows={int(sel.sum())} err={err:.3e}", flush=True)
+    print(f"  buckets={s} valid rows={int(sel.sum())} err={err:.3e}", flush=True)
     assert err <= G.BF16_TOL, err
     vt = torch.from_numpy(valid).to(G.dev())
     assert torch.equal(flat[~vt], x.reshape(-1, d)[~vt]), "padding rows differ from x"
@@ -401,39 +494,109 @@ def test_padded_bucket_workload_sampled(orc):
     assert torch.equal(packed, flat[vt]), "valid rows differ from the packed entry point"
 
 
+def _chain_layer_check(orc, case, layer, cur, out, mask, full):
+    """Teacher-forced check of one chain layer: the oracle gets the exact bf16
+    input the GPU layer got; layer 1 against the plain bf16 bar, later layers
+    against max(2e-2, 2 x the error of the CPU emulation of the same bf16
+    rounding points)."""
+    from tests import bf16_emulation
+
+    wqkv, wo = case.weights[layer]
+    inp = cur.cpu()
+    sel = mask.astype(bool)
+    ref = orc.block_mhsa(inp, case.cu, wqkv, wo, case.block_frames, case.heads,
+                         mask=None if full else mask)
+    emu = bf16_emulation.block_mhsa_rows(inp, case.cu, wqkv, wo, case.block_frames, case.heads,
+                                         mask)
+    err = G.rel_err(out.double().cpu().numpy()[sel], ref[sel])
+    err_emu = G.rel_err(emu[sel], ref[sel])
+    bar = G.BF16_TOL if layer == 0 else max(G.BF16_TOL, 2.0 * err_emu)
+    rms = float(np.sqrt(np.mean(ref[sel] ** 2)))
+    print(f"  layer {layer + 1:2d} ({'all' if full else int(sel.sum())} rows): "
+          f"rms(out)={rms:.3f} err={err:.3e} emulated={err_emu:.3e} bar={bar:.3e}", flush=True)
+    assert np.isfinite(err) and err <= bar, (layer, err, bar)
+
+
 def test_workload_chain16_teacher_forced(orc):
     """16 layers with independent weights, each fed the previous layer's GPU output.
 
     Without normalisation the chain amplifies: activations grow layer by layer
     and the softmax sharpens, so the rounding of Q and K to bf16 alone moves
     later layers' outputs by more than 2e-2 of their RMS.  Each layer is
-    therefore checked teacher-forced (the oracle gets the exact bf16 input the
-    GPU layer got), layer 1 against the plain bf16 bar and every later layer
-    against max(2e-2, 2 x the error of a CPU emulation of the same bf16
-    rounding points)."""
-    from tests import bf16_emulation
-
+    therefore checked teacher-forced on sampled blocks (first, last, two
+    tails, three random); layers 1, 8 and 16 on every row in the test after
+    this one."""
     G.print_case("bf16_b128_chain16")
     case = workloads.build_case(workloads.WORKLOADS["bf16_b128_chain16"])
     assert len(case.weights) == 16
-    mask = G.sample_mask(case.lengths, case.block_frames, n_random=3, seed=2)
-    sel = mask.astype(bool)
+    sampled = G.sample_mask(case.lengths, case.block_frames, n_random=3, seed=2)
     cu = torch.from_numpy(case.cu).to(G.dev())
     cur = case.x.to(G.dev())
     for layer, (wqkv, wo) in enumerate(case.weights):
         out = G.run(cur, cu, wqkv.to(G.dev()), wo.to(G.dev()), case.block_frames, case.heads)
-        inp = cur.cpu()
-        ref = orc.block_mhsa(inp, case.cu, wqkv, wo, case.block_frames, case.heads, mask=mask)
-        emu = bf16_emulation.block_mhsa_rows(inp, case.cu, wqkv, wo, case.block_frames, case.heads,
-                                             mask)
-        err = G.rel_err(out.double().cpu().numpy()[sel], ref[sel])
-        err_emu = G.rel_err(emu[sel], ref[sel])
-        bar = G.BF16_TOL if layer == 0 else max(G.BF16_TOL, 2.0 * err_emu)
-        rms = float(np.sqrt(np.mean(ref[sel] ** 2)))
-        print(f"  layer {layer + 1:2d}: rms(out)={rms:.3f} err={err:.3e} emulated={err_emu:.3e} "
-              f"bar={bar:.3e}", flush=True)
-        assert np.isfinite(err) and err <= bar, (layer, err, bar)
+        _chain_layer_check(orc, case, layer, cur, out, sampled, full=False)
         cur = out
+
+
+@pytest.mark.parametrize("layer", [0, 7, 15])
+def test_workload_chain16_full_layer(orc, layer):
+    """The chain run on the GPU up to `layer`, whose every row is then
+    checked teacher-forced (as in the sampled test above)."""
+    G.print_case("bf16_b128_chain16 full layer", layer=layer + 1)
+    case = workloads.build_case(workloads.WORKLOADS["bf16_b128_chain16"])
+    cu = torch.from_numpy(case.cu).to(G.dev())
+    cur = case.x.to(G.dev())
+    for wqkv, wo in case.weights[:layer]:
+        cur = G.run(cur, cu, wqkv.to(G.dev()), wo.to(G.dev()), case.block_frames, case.heads)
+    wqkv, wo = case.weights[layer]
+    out = G.run(cur, cu, wqkv.to(G.dev()), wo.to(G.dev()), case.block_frames, case.heads)
+    _chain_layer_check(orc, case, layer, cur, out, np.ones(case.n_frames, np.uint8), full=True)
+
+
+def test_chain16_free_running(orc):
+    """The 16-layer chain run free on both sides: the GPU chain (bf16, and
+    the fp32 path on the same values widened) against the oracle's own fp64
+    chain from the same input, layer by layer.  Reported, not gated beyond
+    layer 1: without normalisation the chain amplifies rounding, so even
+    fp32 against fp64 drifts by layer 16 (that drift is the baseline the
+    bf16 number is read against).
+
+    Blocks are the same in every layer and a block's rows depend only on
+    that block's rows of the layer below, so the oracle runs the chain on
+    24 sampled blocks cut out as sequences of their own (the same values
+    bit for bit as in the packed batch, which a pin of the oracle fixes),
+    while the GPU runs the whole batch in the benchmark's configuration."""
+    G.print_case("bf16_b128_chain16 free-running")
+    case = workloads.build_case(workloads.WORKLOADS["bf16_b128_chain16"])
+    bt = accounting.block_table(case.lengths, case.block_frames)
+    rng = np.random.default_rng(4)
+    tails = [i for i, (_, l) in enumerate(bt) if l < case.block_frames]
+    pick = sorted({0, len(bt) - 1, tails[0], tails[-1],
+                   *map(int, rng.choice(len(bt), size=20, replace=False))})
+    rows = np.concatenate([np.arange(bt[i][0], bt[i][0] + bt[i][1]) for i in pick])
+    sub_cu = np.concatenate([[0], np.cumsum([bt[i][1] for i in pick])]).astype(np.int32)
+    cu = torch.from_numpy(case.cu).to(G.dev())
+    gpu = {}
+    for dt in (torch.bfloat16, torch.float32):
+        cur = case.x.to(G.dev()).to(dt)
+        outs = []
+        for wqkv, wo in case.weights:
+            cur = G.run(cur, cu, wqkv.to(G.dev()).to(dt), wo.to(G.dev()).to(dt),
+                        case.block_frames, case.heads)
+            outs.append(cur[torch.from_numpy(rows).to(G.dev())].double().cpu().numpy())
+        gpu[dt] = outs
+    ref = case.x.double().numpy()[rows]
+    print(f"  {len(pick)} blocks, {len(rows)} rows", flush=True)
+    for layer, (wqkv, wo) in enumerate(case.weights):
+        ref = orc.block_mhsa(ref, sub_cu, wqkv, wo, case.block_frames, case.heads)
+        e16 = G.rel_err(gpu[torch.bfloat16][layer], ref)
+        e32 = G.rel_err(gpu[torch.float32][layer], ref)
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        print(f"  layer {layer + 1:2d}: rms(out)={rms:.3f} bf16 err={e16:.3e} "
+              f"fp32 err={e32:.3e}", flush=True)
+        if layer == 0:
+            assert e16 <= G.BF16_TOL and e32 <= G.F32_TOL, (e16, e32)
+        assert np.isfinite(e32)
 
 
 # ---------------------------------------------------------------------------
@@ -499,6 +662,81 @@ def test_in_place_matches_out_of_place(dtype):
     y = x.clone()
     G.run(y, cu, wqkv, wo, 200, 4, out=y)
     assert torch.equal(y, ref)
+
+
+@pytest.mark.parametrize("lengths,d,H", [
+    ([300], 1024, 8), ([300], 384, 3),              # (M - 1) mod 256 = 43
+    ([16999, 1], 1024, 8), ([16999, 1], 384, 3),    # out_proj's second launch: 616 rows
+])
+def test_in_place_ragged_last_panel(lengths, d, H):
+    """out == x where the last 256-row panel holds fewer than 129 rows: the
+    second wave group's rows are then all past the end.  d = 1024 runs the
+    two-wave GEMM, d = 384 the one-wave GEMM; bit for bit equal to the
+    out-of-place result."""
+    G.print_case("in_place_ragged", lengths=lengths, d=d, H=H)
+    case = workloads.custom_case(lengths, d, H, 200, torch.bfloat16, seed=len(lengths) + d)
+    x, cu, wqkv, wo = G.on_dev(case)
+    ref = G.run(x, cu, wqkv, wo, 200, H)
+    for _ in range(3):
+        y = x.clone()
+        G.run(y, cu, wqkv, wo, 200, H, out=y)
+        assert torch.equal(y, ref)
+
+
+def test_in_place_headline_batch():
+    """The headline batch (55 093 frames) in place, as the benchmark sizes it:
+    out_proj's second launch covers 5 941 rows, (5 941 - 1) mod 256 = 52."""
+    case = workloads.build_case(workloads.WORKLOADS[workloads.HEADLINE])
+    G.print_case("in_place_headline", frames=case.n_frames)
+    x, cu, wqkv, wo = G.on_dev(case)
+    ref = G.run(x, cu, wqkv, wo, case.block_frames, case.heads)
+    for _ in range(3):
+        y = x.clone()
+        G.run(y, cu, wqkv, wo, case.block_frames, case.heads, out=y)
+        assert torch.equal(y, ref)
+
+
+def test_stage_out_proj_in_place():
+    """gs_out_proj_residual with out == x over 17 000 rows (two launches,
+    the second of 616 rows) equals the out-of-place result bit for bit."""
+    G.print_case("stage_out_proj_in_place")
+    n = 17000
+    case = workloads.custom_case([n], 1024, 8, 200, torch.bfloat16, seed=6)
+    g = torch.Generator().manual_seed(7)
+    o = torch.randn(n, 1024, generator=g).to(torch.bfloat16).to(G.dev())
+    x, _, _, wo = G.on_dev(case)
+    ref = gsattn.out_proj_residual(o, wo, x)
+    for _ in range(3):
+        y = x.clone()
+        gsattn.out_proj_residual(o, wo, y, out=y)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+
+
+def test_block_attn_long_block_addresses(orc):
+    """One 87 390-row block at d = 8 192 (64 heads): the key rows of its last,
+    partial chunk lie more than 2^31 elements past the block's first row
+    (87 389 * 3 * 8 192 > 2^31), beyond a 32-bit offset.  Sampled query rows
+    of the first and last head against the oracle on that head's columns."""
+    d, H, L = 8192, 64, 87390
+    assert (L - 1) * 3 * d > 2 ** 31 and L % 32 != 0
+    G.print_case("long_block_addresses", d=d, H=H, L=L)
+    g = torch.Generator(device=G.dev()).manual_seed(21)
+    qkv = torch.randn(L, 3 * d, generator=g, device=G.dev(), dtype=torch.bfloat16)
+    cu = torch.tensor([0, L], dtype=torch.int32, device=G.dev())
+    o = gsattn.block_attn(qkv, cu, H, L)
+    torch.cuda.synchronize()
+    rows = [0, 1, 223, 224, L // 2, L - 31, L - 2, L - 1]
+    mask = np.zeros(L, np.uint8)
+    mask[rows] = 1
+    for h in (0, H - 1):
+        cols = torch.cat([torch.arange(j * d + h * 128, j * d + (h + 1) * 128) for j in range(3)])
+        qkv_h = qkv[:, cols.to(G.dev())].cpu()
+        ref = orc.block_attn(qkv_h, np.array([0, L], np.int32), 1, L, mask=mask)
+        got = o[rows, h * 128:(h + 1) * 128].double().cpu().numpy()
+        err = G.rel_err(got, ref[rows])
+        print(f"  head {h}: err={err:.3e}", flush=True)
+        assert err <= G.BF16_TOL, (h, err)
 
 
 def test_block_permutation_equivariance():
