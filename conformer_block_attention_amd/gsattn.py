@@ -235,22 +235,20 @@ def window_xattn_fwd(hcat: torch.Tensor, cu_seqlens: torch.Tensor, xq: torch.Ten
 
 
 def bpe_pool_ctc_greedy(logits: torch.Tensor, blank_prob: torch.Tensor, cu_seqlens: torch.Tensor,
-                        num_classes: int, window: int = 4, stride: int = 2,
-                        num_positions: Optional[int] = None, workspace=None, stream=None,
-                        out=None):
+                        num_classes: int, num_positions: int, window: int = 4, stride: int = 2,
+                        workspace=None, stream=None, out=None):
     """Pooled argmax and CTC greedy tokens.  logits [N, ld] bf16 (the first
-    num_classes columns are the classes), blank_prob [N] fp32.  Returns
-    (argmax [P], tokens [P], token_counts [S]) int32 device tensors; sequence
-    s's tokens start at its first position (the prefix sum of the position
-    counts)."""
+    num_classes columns are the classes), blank_prob [N] fp32, num_positions
+    the pooled positions of all sequences (sum of ceil(len / stride), or
+    more).  Returns (argmax [P], tokens [P], token_counts [S]) int32 device
+    tensors; sequence s's tokens start at its first position (the prefix sum
+    of the position counts)."""
     lib = load()
     n, ld = logits.shape
     s = int(cu_seqlens.numel()) - 1
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
-    if num_positions is None:  # (reads cu_seqlens on the host)
-        ln = torch.diff(cu_seqlens.cpu().long())
-        num_positions = int(((ln + stride - 1) // stride).sum())
+    num_positions = int(num_positions)
     dev = logits.device
     if out is None:
         out = (torch.empty(max(num_positions, 1), dtype=torch.int32, device=dev),

@@ -32,6 +32,20 @@ def build(src: str = SRC, out: str = LIB, extra=()) -> str:
     return out
 
 
+def host_threads() -> int:
+    """Threads the oracle runs on by default: the cores this process may use
+    (its CPU affinity), or OMP_NUM_THREADS where the machine sets it to the
+    share of cores allotted to the job.  The result is the same bits at any
+    thread count."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # (no affinity call on this platform)
+        return os.cpu_count() or 1
+
+
 _P = ctypes.c_void_p
 _I32, _I64 = ctypes.c_int32, ctypes.c_int64
 
@@ -84,7 +98,7 @@ class Oracle:
 
     @staticmethod
     def threads(n: Optional[int]) -> int:
-        return int(n) if n else (os.cpu_count() or 1)
+        return int(n) if n else host_threads()
 
     @staticmethod
     def _check(rc: int, what: str):

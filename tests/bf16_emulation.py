@@ -31,7 +31,9 @@ def _bf16(a: np.ndarray) -> np.ndarray:
 
 def block_mhsa_rows(x, cu, wqkv, wo, block_frames: int, heads: int, mask: np.ndarray) -> np.ndarray:
     """Emulated output for the rows of every block that has a row selected in
-    `mask` (NaN elsewhere).  x, wqkv, wo: bf16 torch tensors on the CPU."""
+    `mask` (NaN elsewhere).  x, wqkv, wo: bf16 torch tensors on the CPU.
+    The projections run over all of those rows at once; the attention block
+    by block."""
     xd = x.double().numpy()
     w1 = wqkv.double().numpy()
     w2 = wo.double().numpy()
@@ -39,20 +41,26 @@ def block_mhsa_rows(x, cu, wqkv, wo, block_frames: int, heads: int, mask: np.nda
     dh = d // heads
     out = np.full((n, d), np.nan)
     cu = np.asarray(cu, dtype=np.int64)
+    spans = []
     for s in range(len(cu) - 1):
         for a in range(int(cu[s]), int(cu[s + 1]), block_frames):
             b = min(a + block_frames, int(cu[s + 1]))
-            if not mask[a:b].any():
-                continue
-            xb = xd[a:b]
-            qkv = _bf16(xb @ w1.T)
-            o = np.empty((b - a, d))
-            for h in range(heads):
-                q = qkv[:, h * dh:(h + 1) * dh]
-                k = qkv[:, d + h * dh:d + (h + 1) * dh]
-                v = qkv[:, 2 * d + h * dh:2 * d + (h + 1) * dh]
-                z = (q @ k.T) / math.sqrt(dh)
-                p = _bf16(np.exp(z - z.max(axis=1, keepdims=True)))
-                o[:, h * dh:(h + 1) * dh] = (p @ v) / p.sum(axis=1, keepdims=True)
-            out[a:b] = _bf16(xb + _bf16(o) @ w2.T)
+            if mask[a:b].any():
+                spans.append((a, b))
+    if not spans:
+        return out
+    rows = np.concatenate([np.arange(a, b) for a, b in spans])
+    xs = xd[rows]
+    qkv = _bf16(xs @ w1.T)
+    o = np.empty((len(rows), d))
+    p0 = 0
+    for a, b in spans:
+        L = b - a
+        blk = qkv[p0:p0 + L].reshape(L, 3, heads, dh).transpose(1, 2, 0, 3)  # [3][H][L][dh]
+        q, k, v = blk[0], blk[1], blk[2]
+        z = (q @ k.transpose(0, 2, 1)) / math.sqrt(dh)                      # [H][L][L]
+        p = _bf16(np.exp(z - z.max(axis=2, keepdims=True)))
+        o[p0:p0 + L] = ((p @ v) / p.sum(axis=2, keepdims=True)).transpose(1, 0, 2).reshape(L, d)
+        p0 += L
+    out[rows] = _bf16(xs + _bf16(o) @ w2.T)
     return out

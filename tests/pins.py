@@ -479,4 +479,63 @@ def pin_ctc_pool_constructed(orc):
     assert [g.tolist() for g in got] == want, (got, want)
 
 
+def pooled_scores_f64(logits, blank_prob, lengths, window=4, stride=2):
+    """Pooled class scores in fp64 straight from the definition (model card,
+    "Model Architecture" (1): windows of `window` frames weighted by
+    1 - blank probability; stride 2 from the ONNX export's 211 positions for
+    422 frames), and the fp32 rounding bound of each: a pooled score sums at
+    most `window` products w_t * l_t with w_t = 1 - b_t, and the fp32 order
+    rounds w_t, each product and each partial sum once, so
+    |s32 - s64| <= g * sum_t |w_t l_t|, g = n u / (1 - n u), n = window + 2,
+    u = 2^-24 (the forward error bound of a recursive sum).
+    Returns (scores [P, C], bound [P, C])."""
+    logits = np.asarray(logits, np.float64)
+    w = 1.0 - np.asarray(blank_prob, np.float64)
+    u = 2.0 ** -24
+    n = window + 2
+    g = n * u / (1 - n * u)
+    scores, bounds = [], []
+    first = 0
+    for ln in lengths:
+        for start in range(0, ln, stride):
+            rows = np.arange(first + start, first + min(start + window, ln))
+            terms = w[rows, None] * logits[rows]
+            scores.append(terms.sum(axis=0))
+            bounds.append(g * np.abs(terms).sum(axis=0))
+        first += ln
+    c = logits.shape[1]
+    return (np.asarray(scores).reshape(-1, c), np.asarray(bounds).reshape(-1, c))
+
+
+def decisive(scores, bounds):
+    """Positions whose fp64 winner beats every other class by more than the
+    two rounding bounds together (there, any order of fp32 rounding picks the
+    same class), and the fp64 winners."""
+    top = np.argmax(scores, axis=1)
+    rows = np.arange(len(top))
+    lead = scores[rows, top][:, None] - scores - (bounds[rows, top][:, None] + bounds)
+    lead[rows, top] = np.inf
+    return lead.min(axis=1) > 0, top
+
+
+def pin_ctc_pool_fp64_margin(orc):
+    """The oracle's fp32-order argmax equals the argmax of fp64 pooled scores
+    computed from the definition wherever the fp64 lead exceeds the fp32
+    rounding bound (and such positions are nearly all of them)."""
+    from oracle import ctc_pool as cp
+    rng = np.random.default_rng(31)
+    lengths, classes = [41, 1, 0, 30, 2], 3000
+    n = sum(lengths)
+    logits = torch.from_numpy(rng.standard_normal((n, classes)).astype(np.float32)).to(
+        torch.bfloat16).float().numpy()
+    logits[:, 0] += 1.0
+    bp = rng.uniform(0, 1, n).astype(np.float32)
+    got = cp.pooled_argmax(logits, bp, np.concatenate([[0], np.cumsum(lengths)]))
+    s64, bound = pooled_scores_f64(logits, bp, lengths)
+    ok, top = decisive(s64, bound)
+    assert len(got) == len(top) == int(cp.positions(lengths).sum())
+    assert ok.mean() > 0.9
+    assert np.array_equal(got[ok], top[ok])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -21,8 +21,9 @@ def _run(logits_f32, bp, lengths, classes, ld, window=4, stride=2):
     dev = G.dev()
     lg = torch.from_numpy(pad).to(torch.bfloat16).to(dev)
     cu = torch.from_numpy(workloads.cu_seqlens(lengths)).to(dev)
+    npos = int(cp.positions(lengths, stride).sum())
     am, tok, cnt = gsattn.bpe_pool_ctc_greedy(lg, torch.from_numpy(np.asarray(bp, np.float32)).to(dev),
-                                              cu, classes, window=window, stride=stride)
+                                              cu, classes, npos, window=window, stride=stride)
     torch.cuda.synchronize()
     return am.cpu().numpy(), tok.cpu().numpy(), cnt.cpu().numpy()
 
@@ -78,33 +79,42 @@ def test_ctc_pool_ties_go_to_the_lowest_class():
     assert np.array_equal(am, ref)
 
 
-def test_ctc_pool_full_size_sampled():
+def test_ctc_pool_full_size():
     """The benchmark's workload (55 093 frames of 100 353 classes, rows of
-    100 360): sampled positions against the oracle exactly (their frames
-    copied back), tokens of three sequences exactly, run-to-run equality."""
+    100 360): every pooled position's argmax and every sequence's tokens
+    against the oracle exactly (each sequence's frames copied back in turn),
+    run-to-run equality."""
     lengths = workloads.WORKLOADS["bf16_b128_lognormal"].lengths()
     logits, bp, cu = workloads.bpe_inputs(lengths)
     G.print_case("ctc full", frames=int(cu[-1]), classes=workloads.BPE_CLASSES)
-    am, tok, cnt = gsattn.bpe_pool_ctc_greedy(logits, bp, cu, workloads.BPE_CLASSES)
-    am2, tok2, cnt2 = gsattn.bpe_pool_ctc_greedy(logits, bp, cu, workloads.BPE_CLASSES)
+    npos = cp.positions(lengths)
+    p = int(npos.sum())
+    am, tok, cnt = gsattn.bpe_pool_ctc_greedy(logits, bp, cu, workloads.BPE_CLASSES, p)
+    am2, tok2, cnt2 = gsattn.bpe_pool_ctc_greedy(logits, bp, cu, workloads.BPE_CLASSES, p)
     torch.cuda.synchronize()
     assert torch.equal(am, am2) and torch.equal(cnt, cnt2)
     am, tok, cnt = am.cpu().numpy(), tok.cpu().numpy(), cnt.cpu().numpy()
-    npos = cp.positions(lengths)
     first = np.concatenate([[0], np.cumsum(npos)])
     # (entries past a sequence's token count are unspecified)
     tok2 = tok2.cpu().numpy()
     for s in range(len(lengths)):
         assert np.array_equal(tok[first[s]:first[s] + cnt[s]], tok2[first[s]:first[s] + cnt[s]])
     cuh = workloads.cu_seqlens(lengths)
-    for s in (0, len(lengths) // 2, len(lengths) - 1):
+    bph = bp.cpu().numpy()
+    near = 0
+    for s in range(len(lengths)):
         a, b = int(cuh[s]), int(cuh[s + 1])
         lg = logits[a:b, :workloads.BPE_CLASSES].float().cpu().numpy()
-        ref = cp.pooled_argmax(lg, bp[a:b].cpu().numpy(), [0, b - a])
+        ref = cp.pooled_argmax(lg, bph[a:b], [0, b - a])
         assert np.array_equal(am[first[s]:first[s + 1]], ref), s
         want = cp.ctc_greedy(ref, [len(ref)])[0].tolist()
         assert tok[first[s]:first[s] + cnt[s]].tolist() == want, s
-    print(f"  positions={int(first[-1])} tokens={int(cnt.sum())}", flush=True)
+        # the fp32 decision against fp64 pooled scores: equal outside near-ties
+        ok, top = pins.decisive(*pins.pooled_scores_f64(lg, bph[a:b], [b - a]))
+        assert np.array_equal(am[first[s]:first[s + 1]][ok], top[ok]), s
+        near += int((~ok).sum())
+    print(f"  sequences={len(lengths)} positions={int(first[-1])} tokens={int(cnt.sum())} "
+          f"fp64 near-ties={near}", flush=True)
 
 
 def test_ctc_pool_num_positions_past_the_count():
@@ -119,9 +129,8 @@ def test_ctc_pool_num_positions_past_the_count():
     dev = G.dev()
     cu = torch.from_numpy(workloads.cu_seqlens(lengths)).to(dev)
     p = int(cp.positions(lengths).sum())
-    a1, t1, c1 = gsattn.bpe_pool_ctc_greedy(logits.to(dev), bp.to(dev), cu, classes)
-    a2, t2, c2 = gsattn.bpe_pool_ctc_greedy(logits.to(dev), bp.to(dev), cu, classes,
-                                            num_positions=p + 3)
+    a1, t1, c1 = gsattn.bpe_pool_ctc_greedy(logits.to(dev), bp.to(dev), cu, classes, p)
+    a2, t2, c2 = gsattn.bpe_pool_ctc_greedy(logits.to(dev), bp.to(dev), cu, classes, p + 3)
     torch.cuda.synchronize()
     assert torch.equal(a2[:p], a1) and a2[p:].tolist() == [0, 0, 0]
     assert torch.equal(c2, c1)

@@ -67,10 +67,10 @@ def test_window_xattn_in_place():
     assert torch.equal(out, ref)
 
 
-def test_window_xattn_full_size_sampled():
+def test_window_xattn_full_size():
     """The benchmark's workload and launch configuration (55 093 frames of
-    4 096 features, 3 730 windows of 3 queries, dq = 2 048, 16 heads): 40
-    windows against the oracle, run-to-run bit equality, and a sequence run
+    4 096 features, 3 730 windows of 3 queries, dq = 2 048, 16 heads): every
+    window against the oracle, run-to-run bit equality, and a sequence run
     alone gives the bits it gets in the batch."""
     name = "bf16_qformer_xattn_b128"
     c = workloads.build_xattn_case(workloads.XATTN_WORKLOADS[name])
@@ -78,12 +78,10 @@ def test_window_xattn_full_size_sampled():
     out = _run(c)
     assert torch.equal(out, _run(c)), "run-to-run results differ"
     nw = c.xq.shape[0]
-    rng = np.random.default_rng(7)
-    pick = sorted({0, nw - 1, *map(int, rng.choice(nw, size=38, replace=False))})
-    ref = _ref(c, windows=pick)
+    ref = _ref(c)
     got = out.double().cpu().numpy()
-    err = G.rel_err(got[pick], ref[pick])
-    print(f"  sampled windows={len(pick)} err={err:.3e}", flush=True)
+    err = G.rel_err(got, ref)
+    print(f"  windows={nw} err={err:.3e}", flush=True)
     assert err <= G.BF16_TOL, err
     # sequence 5 alone: its windows are a contiguous run of the batch's
     s = 5
