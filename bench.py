@@ -2,7 +2,10 @@
 
 One step = one call of gs_block_mhsa_fwd (Q|K|V projection, block attention,
 output projection with residual) over the whole packed batch, inputs already
-resident in HBM.  Prints one JSON line.
+resident in HBM.  Prints one JSON line.  The step time is the median over the
+timed steps of the GPU time from a step's first kernel to its last (HIP
+events the library records on the launch stream), with p10, p90, the mean
+and the wall-clock mean beside it; per-kernel times are means.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
   python bench.py --copy-calibration MB   (plain device copy of MB MiB, for
@@ -70,7 +73,7 @@ def cpu_baseline(case, budget_s: float = 12.0):
     import oracle
 
     orc = oracle.load()
-    nthreads = min(os.cpu_count() or 1, 16)
+    nthreads = oracle.host_threads()
     wqkv, wo = case.weights[0]
     w1, w2 = wqkv.double().numpy(), wo.double().numpy()
     frames = 0
@@ -228,8 +231,7 @@ def bench_ctc(args):
                      device=dev)
 
     def step():
-        gsattn.bpe_pool_ctc_greedy(logits, bp, cu, classes, num_positions=npos, workspace=ws,
-                                   out=out)
+        gsattn.bpe_pool_ctc_greedy(logits, bp, cu, classes, npos, workspace=ws, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -280,6 +282,79 @@ def bench_ctc(args):
     print(json.dumps(rec), flush=True)
 
 
+# kernel roles by name (rocprofv3 reports template arguments in the name)
+KERNEL_ROLES = (
+    ("gemm_pp_bf16_kernel<256, false", "qkv_proj"),
+    ("gemm_pp_bf16_kernel<256, true", "out_proj"),
+    ("gemm_bf16_nt_kernel<64, 128, 64, 3, false, 0, 4, false>", "qkv_proj (last rows)"),
+    ("gemm_bf16_nt_kernel<192, 128, 64, 3, false, 0, 4, true>", "out_proj (last rows)"),
+    ("block_attn_bf16_kernel", "block_attn"),
+    ("build_unit_table_kernel", "(attention work-unit table)"),
+)
+CUS, SIMDS_PER_CU = 256, 4
+
+
+def _role(kernel_name: str) -> str:
+    for key, role in KERNEL_ROLES:
+        if key in kernel_name:
+            return role
+    return kernel_name.split("(")[0]
+
+
+def counter_summary(outdir: str) -> dict:
+    """Per-kernel averages of the counters in rocprofv3's CSV output under
+    `outdir` (any *counter_collection.csv, joined by dispatch to the
+    *kernel_trace.csv beside it), with derived figures:
+      mfma_busy   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs)
+      clock_mhz   = GRBM_GUI_ACTIVE / duration (GRBM_GUI_ACTIVE divided by
+                    the XCD count first when the counter sums the 8 XCDs)
+      mfma_flop   = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+      lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+    """
+    import csv
+    import glob
+
+    dur = {}
+    for f in glob.glob(os.path.join(outdir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            dur[(f.rsplit("kernel_trace.csv", 1)[0], r["Dispatch_Id"])] = (
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    acc = {}
+    for f in glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True):
+        pre = f.rsplit("counter_collection.csv", 1)[0]
+        for r in csv.DictReader(open(f)):
+            k = _role(r["Kernel_Name"])
+            e = acc.setdefault(k, {"dispatches": set(), "ns": {}, "counters": {}})
+            did = r["Dispatch_Id"]
+            e["dispatches"].add((pre, did))
+            if (pre, did) in dur:
+                e["ns"][(pre, did)] = dur[(pre, did)]
+            c = e["counters"].setdefault(r["Counter_Name"], {})
+            c[(pre, did)] = c.get((pre, did), 0.0) + float(r["Counter_Value"])
+    out = {}
+    for k, e in acc.items():
+        avg = {n: sum(v.values()) / len(v) for n, v in e["counters"].items()}
+        rec = {"dispatches": len(e["dispatches"]), "counters": avg}
+        if e["ns"]:
+            rec["avg_us"] = sum(e["ns"].values()) / len(e["ns"]) / 1e3
+        g = avg.get("GRBM_GUI_ACTIVE")
+        if g and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            rec["mfma_busy"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * CUS * SIMDS_PER_CU)
+        if g and e["ns"]:
+            # per-dispatch ratio of active cycles to nanoseconds
+            ratios = [e["counters"]["GRBM_GUI_ACTIVE"][d] / e["ns"][d]
+                      for d in e["ns"] if d in e["counters"]["GRBM_GUI_ACTIVE"] and e["ns"][d]]
+            mhz = 1e3 * sum(ratios) / len(ratios)
+            rec["grbm_cycles_per_ns"] = mhz / 1e3
+            rec["clock_mhz"] = mhz / 8 if mhz > 5000 else mhz
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+            rec["mfma_flop"] = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        if avg.get("SQ_LDS_IDX_ACTIVE"):
+            rec["lds_conflict"] = avg.get("SQ_LDS_BANK_CONFLICT", 0.0) / avg["SQ_LDS_IDX_ACTIVE"]
+        out[k] = rec
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,7 +367,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB MiB, 5 times")
+    ap.add_argument("--counter-summary", default="", metavar="DIR",
+                    help="only summarise the rocprofv3 counter CSVs under DIR (no GPU)")
     args = ap.parse_args()
+
+    if args.counter_summary:
+        print(json.dumps(counter_summary(args.counter_summary), indent=1, sort_keys=True))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -375,12 +456,17 @@ def main():
         per["block_attn"].append(ev.elapsed_ms(b + 1, b + 2))
         per["out_proj"].append(ev.elapsed_ms(b + 2, b + 3))
     avg_ms = {k: float(np.mean(v)) for k, v in per.items()}
+    # one step on the GPU: from the first kernel of its first layer to the end
+    # of the last kernel of its last layer
+    step_ms = np.array([ev.elapsed_ms(4 * nl * k, 4 * nl * k + 4 * (nl - 1) + 3)
+                        for k in range(args.steps)])
+    p10, p50, p90 = (float(v) for v in np.percentile(step_ms, [10, 50, 90]))
 
-    ms_step = el / args.steps * 1e3
+    ms_step = p50
     valid = int(np.sum(case.lengths))  # frames (padding rows excluded)
-    frames_per_s = valid * nl / (el / args.steps)  # frame-layers per second
+    frames_per_s = valid * nl / (ms_step * 1e-3)  # frame-layers per second
     fl = accounting.useful_flops(case.lengths, d, case.block_frames)
-    tflops = fl["total"] * nl / (el / args.steps) / 1e12
+    tflops = fl["total"] * nl / (ms_step * 1e-3) / 1e12
     bf16 = x.dtype == torch.bfloat16
     peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
     elem = 2 if bf16 else 4
@@ -419,6 +505,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "step_ms": {"median": p50, "p10": p10, "p90": p90, "mean": float(np.mean(step_ms)),
+                    "wall_mean": el / args.steps * 1e3},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
