@@ -291,7 +291,7 @@ KERNEL_ROLES = (
     ("block_attn_bf16_kernel", "block_attn"),
     ("build_unit_table_kernel", "(attention work-unit table)"),
 )
-CUS, SIMDS_PER_CU = 256, 4
+CUS, SIMDS_PER_CU, XCDS = 256, 4, 8
 
 
 def _role(kernel_name: str) -> str:
@@ -304,13 +304,18 @@ def _role(kernel_name: str) -> str:
 def counter_summary(outdir: str) -> dict:
     """Per-kernel averages of the counters in rocprofv3's CSV output under
     `outdir` (any *counter_collection.csv, joined by dispatch to the
-    *kernel_trace.csv beside it), with derived figures:
-      mfma_busy   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs)
-      clock_mhz   = GRBM_GUI_ACTIVE / duration (GRBM_GUI_ACTIVE divided by
-                    the XCD count first when the counter sums the 8 XCDs)
+    *kernel_trace.csv beside it), with derived figures.  rocprofv3 sums a
+    counter over its hardware instances, so GRBM_GUI_ACTIVE comes as the sum
+    of the 8 XCDs' active cycles; per XCD it is the kernel's cycle count:
+      cycles      = GRBM_GUI_ACTIVE / 8
+      clock_mhz   = cycles / duration
+      mfma_busy   = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)
+                    (the busy count is summed over SIMDs; a 32x32x16 bf16
+                    product counts 32 cycles, a 16x16x32 one 16)
       mfma_flop   = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
       lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
-    """
+    GRBM_GUI_ACTIVE also counts a few microseconds around each dispatch, so
+    the clock of a kernel much shorter than 100 us reads high."""
     import csv
     import glob
 
@@ -338,15 +343,15 @@ def counter_summary(outdir: str) -> dict:
         if e["ns"]:
             rec["avg_us"] = sum(e["ns"].values()) / len(e["ns"]) / 1e3
         g = avg.get("GRBM_GUI_ACTIVE")
+        if g:
+            rec["cycles"] = g / XCDS
         if g and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
-            rec["mfma_busy"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * CUS * SIMDS_PER_CU)
+            rec["mfma_busy"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (g / XCDS * CUS * SIMDS_PER_CU)
         if g and e["ns"]:
             # per-dispatch ratio of active cycles to nanoseconds
-            ratios = [e["counters"]["GRBM_GUI_ACTIVE"][d] / e["ns"][d]
+            ratios = [e["counters"]["GRBM_GUI_ACTIVE"][d] / XCDS / e["ns"][d]
                       for d in e["ns"] if d in e["counters"]["GRBM_GUI_ACTIVE"] and e["ns"][d]]
-            mhz = 1e3 * sum(ratios) / len(ratios)
-            rec["grbm_cycles_per_ns"] = mhz / 1e3
-            rec["clock_mhz"] = mhz / 8 if mhz > 5000 else mhz
+            rec["clock_mhz"] = 1e3 * sum(ratios) / len(ratios)
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
             rec["mfma_flop"] = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
         if avg.get("SQ_LDS_IDX_ACTIVE"):
