@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gsattn.h"
 #include "attn_units.hpp"
@@ -142,6 +143,12 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
   }
 }
 }  // namespace gs
+
+// Workspace of gs_block_mhsa_fwd_noalloc: one copy per GPU, held until the
+// process ends.  Host code never uses this name as an address (on the host
+// it only stands for the symbol): scratch_of_current_device() looks up each
+// device's copy with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[GS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -306,6 +313,30 @@ gs_status plan_fwd(const void* x, const void* Wqkv, const void* Wo, int32_t bloc
   return GS_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+gs_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  GS_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GS_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  GS_TRY(hip_status(g_scratch_err[dev], "hipGetSymbolAddress(scratch)"));
+  if (!g_scratch_ptr[dev]) return fail(GS_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+  *ptr = g_scratch_ptr[dev];
+  return GS_OK;
+}
+
 gs_status record(const gs_mhsa_desc* desc, int i, hipStream_t st) {
   if (!desc->kernel_events) return GS_OK;
   return hip_status(hipEventRecord(desc->kernel_events[i], st), "hipEventRecord");
@@ -417,6 +448,25 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
   GS_TRY(gs_out_proj_residual(p.o, Wo, x, out, p.N, p.d, desc->dtype, stream));
   GS_TRY(record(desc, 3, stream));
   return GS_OK;
+}
+
+gs_status gs_block_mhsa_fwd_noalloc(const void* x, const int32_t* cu_seqlens, const void* Wqkv,
+                                    const void* Wo, int32_t block_frames, int32_t heads,
+                                    void* out, hipStream_t stream, int32_t num_seqs,
+                                    int64_t total_frames, int32_t d_model, gs_dtype dtype) {
+  GS_TRY(check_dtype(dtype));
+  GS_TRY(check_dims(total_frames, d_model));
+  const size_t need = gs_block_mhsa_workspace_bytes(total_frames, d_model, dtype);
+  if (need > GS_NOALLOC_SCRATCH_BYTES)
+    return fail(GS_ERR_UNSUPPORTED,
+                "%lld frames at d_model %d need %zu bytes of workspace; the static scratch "
+                "holds %zu",
+                (long long)total_frames, d_model, need, (size_t)GS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  GS_TRY(scratch_of_current_device(&ws));
+  const gs_mhsa_desc desc{num_seqs, total_frames, d_model, dtype, ws, GS_NOALLOC_SCRATCH_BYTES,
+                          nullptr};
+  return gs_block_mhsa_fwd(x, cu_seqlens, Wqkv, Wo, block_frames, heads, out, stream, &desc);
 }
 
 size_t gs_block_mhsa_padded_workspace_bytes(int32_t num_seqs, int32_t bucket_frames,

@@ -21,6 +21,7 @@ GS_F32, GS_BF16 = 0, 1
 
 EXPORTS = (
     "gs_block_mhsa_workspace_bytes", "gs_block_mhsa_fwd", "gs_block_mhsa_fwd_padded",
+    "gs_block_mhsa_fwd_noalloc",
     "gs_block_mhsa_padded_workspace_bytes",
     "gs_qkv_proj", "gs_block_attn",
     "gs_block_attn_workspace_bytes", "gs_out_proj_residual", "gs_status_string",
@@ -81,6 +82,9 @@ def load(path: Optional[str] = None):
     lib.gs_block_mhsa_workspace_bytes.argtypes = [I64, I32, ctypes.c_int]
     lib.gs_block_mhsa_fwd.restype = ctypes.c_int
     lib.gs_block_mhsa_fwd.argtypes = [P, P, P, P, I32, I32, P, P, ctypes.POINTER(_Desc)]
+    lib.gs_block_mhsa_fwd_noalloc.restype = ctypes.c_int
+    lib.gs_block_mhsa_fwd_noalloc.argtypes = [P, P, P, P, I32, I32, P, P, I32, I64, I32,
+                                              ctypes.c_int]
     lib.gs_block_mhsa_padded_workspace_bytes.restype = ctypes.c_size_t
     lib.gs_block_mhsa_padded_workspace_bytes.argtypes = [I32, I32, I32, ctypes.c_int]
     lib.gs_block_mhsa_fwd_padded.restype = ctypes.c_int
@@ -175,6 +179,28 @@ def block_mhsa_fwd(x: torch.Tensor, cu_seqlens: torch.Tensor, wqkv: torch.Tensor
         _dev(x, "x"), _dev(cu_seqlens, "cu_seqlens"), _dev(wqkv, "Wqkv", x.dtype),
         _dev(wo, "Wo", x.dtype), int(block_frames), int(heads), _dev(out, "out", x.dtype),
         _stream(stream), ctypes.byref(desc)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GS_NOALLOC_SCRATCH_BYTES
+
+
+def block_mhsa_fwd_noalloc(x: torch.Tensor, cu_seqlens: torch.Tensor, wqkv: torch.Tensor,
+                           wo: torch.Tensor, block_frames: int, heads: int,
+                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """block_mhsa_fwd with the library's static per-GPU scratch as its
+    workspace (no device allocation by the library; `out` is allocated here
+    only if not given)."""
+    lib = load()
+    n, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check(lib.gs_block_mhsa_fwd_noalloc(
+        _dev(x, "x"), _dev(cu_seqlens, "cu_seqlens"), _dev(wqkv, "Wqkv", x.dtype),
+        _dev(wo, "Wo", x.dtype), int(block_frames), int(heads), _dev(out, "out", x.dtype),
+        _stream(stream), int(cu_seqlens.numel()) - 1, int(n), int(d), _gs_dtype(x.dtype)))
     return out
 
 

@@ -102,6 +102,32 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
                             hipStream_t stream, const gs_mhsa_desc* desc);
 
 /*
+ * gs_block_mhsa_fwd without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The arguments are those of
+ * gs_block_mhsa_fwd with the descriptor's sizes passed directly; the
+ * workspace is a static device array of GS_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - The scratch of the current device (hipGetDevice) is used; `stream`
+ *     must belong to that device.  Its address is looked up once per device
+ *     on the first call there.
+ *   - Sizes whose workspace (gs_block_mhsa_workspace_bytes) exceeds
+ *     GS_NOALLOC_SCRATCH_BYTES return GS_ERR_UNSUPPORTED before anything is
+ *     enqueued: at d_model 1024 that is up to 8 168 bf16 frames (4 089 fp32).
+ *   - Every call on one GPU shares that GPU's scratch and leaves its
+ *     contents behind; calls on one GPU that overlap in time (other streams,
+ *     other threads) race and must be serialised by the caller.
+ * Results are bit for bit those of gs_block_mhsa_fwd with its own workspace.
+ */
+#define GS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gs_status gs_block_mhsa_fwd_noalloc(const void* x, const int32_t* cu_seqlens, const void* Wqkv,
+                                    const void* Wo, int32_t block_frames, int32_t heads,
+                                    void* out, hipStream_t stream, int32_t num_seqs,
+                                    int64_t total_frames, int32_t d_model, gs_dtype dtype);
+
+/*
  * The whole sub-layer on fixed-length padded buckets instead of packed
  * sequences (the fixed [1, 800, features] encoder bucket of the portable
  * INT4 export, README "What Changed" item 4; how its padding is treated is

@@ -111,6 +111,20 @@ def test_stage_argument_errors(lib):
     assert lib.gs_qkv_proj(FAKE, FAKE, FAKE, 1 << 31, 1024, gsattn.GS_BF16, None) == gsattn.GS_ERR_UNSUPPORTED
 
 
+def test_noalloc_refusals_before_any_device_work(lib):
+    """Checks of gs_block_mhsa_fwd_noalloc that need no GPU: a workspace past
+    the static scratch, bad dtype or sizes."""
+    def call(N=400, d=1024, dt=gsattn.GS_BF16, S=2):
+        return lib.gs_block_mhsa_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, 200, 8, FAKE + (1 << 30),
+                                             None, S, N, d, dt)
+    assert call(N=8169) == gsattn.GS_ERR_UNSUPPORTED
+    assert "static scratch" in lib.gs_last_error_detail().decode()
+    assert call(N=4090, dt=gsattn.GS_F32) == gsattn.GS_ERR_UNSUPPORTED
+    assert call(dt=9) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert call(N=-1) == gsattn.GS_ERR_INVALID_ARGUMENT
+    assert call(d=1000) == gsattn.GS_ERR_UNSUPPORTED
+
+
 def _fwd_padded(lib, desc, x=FAKE, lengths=FAKE, T=200, wqkv=FAKE, wo=FAKE, B=200, H=8,
                 out=FAKE + (1 << 30)):
     d = ctypes.byref(desc) if desc is not None else None
