@@ -31,6 +31,7 @@ from conformer_block_attention_amd import accounting, gsattn, workloads  # noqa:
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+NOMINAL_CLOCK_MHZ = 2400.0  # the clock the published peaks are quoted at
 KERNELS = ("qkv_proj", "block_attn", "out_proj")
 HEADLINE_METRIC = "encoder frames/sec through block-MHSA (bf16, B=128 packed); % bf16 MFMA peak"
 KERNEL_SOURCES = {
@@ -65,6 +66,24 @@ def traffic_for(kernel: str, workload: str):
             return None
         return t.get("bytes_per_launch")
     return None
+
+
+def counters_for(kernel: str, workload: str, achieved_tflops: float):
+    """MFMA busy fraction and average clock of the kernel's main launch from
+    the committed rocprofv3 counter runs (profiles/counters_<kernel>.json),
+    if its sources are still those that were measured, with the bf16 peak
+    scaled to that clock and the achieved rate against it."""
+    p = os.path.join(ROOT, "profiles", f"counters_{kernel}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        c = json.load(f)
+    if c.get("workload", "").split(" ")[0] != workload or c.get("source_hash") != source_hash(kernel):
+        return None
+    peak = BF16_PEAK_TFLOPS * c["clock_mhz"] / NOMINAL_CLOCK_MHZ
+    return {"kernel": kernel, "mfma_busy": c["mfma_busy"], "clock_mhz": c["clock_mhz"],
+            "peak_at_clock": peak, "frac_at_clock": achieved_tflops / peak,
+            "source": f"profiles/counters_{kernel}.json"}
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
@@ -527,6 +546,8 @@ def main():
         "useful_gflop_per_layer": fl["total"] / 1e9,
         "kernels": kernels,
         "roofline": roof,
+        "counters": (counters_for(dom, w.name, fl[dom] / (avg_ms[dom] * 1e-3) / 1e12)
+                     if bf16 else None),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
