@@ -26,8 +26,13 @@
 //     barrier makes them visible to all.
 //   * output: a cross-lane swap (v_permlane32_swap) joins lane l's and lane
 //     l+32's 4-column halves of the transposed accumulator tile into 16-byte
-//     row pieces, stored right away.  out_proj loads the residual in the same
-//     piece layout and adds it in fp32 before the one RNE rounding.
+//     row pieces.  Without a residual each wave then transposes its pieces
+//     through 8 KB of LDS (the 32 KB the ring leaves free, one area per wave
+//     of a group; the two groups use them in different phases), so that each
+//     store writes 8 whole 128-byte rows: stores of 32 rows x 32 bytes, the
+//     MFMA layout, cost the projection about 2.5 % more.  out_proj loads the
+//     residual in the piece layout and adds it in fp32 before the one RNE
+//     rounding.
 //   * tile order: all tiles are ordered in groups of 8 panels (256-row
 //     strips), panel fastest within a group.  The 8 XCDs receive workgroup
 //     ids round-robin; each XCD owns one eighth of that order (a contiguous
@@ -157,7 +162,10 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
   constexpr int NOUT = TI * TJ * 2;                 // 16-byte output pieces per lane per tile
   static_assert(BN % 128 == 0 || BN == 384, "tile width");
   static_assert((KK == 1 || KK == 2) && WN % 32 == 0, "phase and tile shape");
-  __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STAGE];
+  // (without a residual: 8 KB per wave of a group after the ring, for the
+  // transpose of finished pieces into whole output rows)
+  constexpr int XT_ELEMS = RESID ? 0 : 4 * 4096;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STAGE + XT_ELEMS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -305,6 +313,41 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
           rres[i * TJ * 2 + q] = __builtin_amdgcn_raw_buffer_load_b128(
               res_rs, ro[i] + ((q >> 1) * 32 + (q & 1) * 16) * 2, 0, 0);
     }
+    if constexpr (!RESID) {
+      // rows of 8 pieces, piece c of row r at c ^ (r mod 8): the 32 rows a
+      // write touches and the 8 pieces a read takes hit distinct banks.  The
+      // wave reads only what it wrote itself (LDS keeps one wave's accesses in
+      // order); the other group uses the area only after the next barrier.
+      GS_LDS u32x4_t* xt = (GS_LDS u32x4_t*)&smem[NST * STAGE] + (wave & 3) * 512;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+              const f32x16& a = acc[h * 2 + ii][j];
+              unsigned x0 = pack_bf16x2(a[gp * 8 + 0], a[gp * 8 + 1]);
+              unsigned x1 = pack_bf16x2(a[gp * 8 + 2], a[gp * 8 + 3]);
+              unsigned y0 = pack_bf16x2(a[gp * 8 + 4], a[gp * 8 + 5]);
+              unsigned y1 = pack_bf16x2(a[gp * 8 + 6], a[gp * 8 + 7]);
+              swap_lo_hi(x0, y0);
+              swap_lo_hi(x1, y1);
+              const int r = ii * 32 + frag_row;
+              const int c8 = j * 4 + gp * 2 + half;
+              xt[r * 8 + (c8 ^ (r & 7))] = u32x4_t{x0, x1, y0, y1};
+            }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int r = s * 8 + (lane >> 3);
+          const int c8 = lane & 7;
+          const u32x4_t v = xt[r * 8 + (c8 ^ (r & 7))];
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, out_rs, (unsigned)((wm * 128 + h * 64 + r) * Nc + wn * WN + c8 * 8) * 2u, 0, 0);
+        }
+      }
+    } else
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
 #pragma unroll

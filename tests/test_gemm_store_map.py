@@ -1,5 +1,6 @@
 """Host-side model of where the projection GEMM's epilogue stores, and what
-it reads as the residual (C = R + A . W^T, with C == R allowed in place).
+it reads as the residual (C = R + A . W^T, with C == R allowed in place);
+and of the LDS transpose the kernel without a residual stores through.
 
 The model follows the two-wave kernel's epilogue: 256 x 256 tiles, wave w
 owns the 128 x 64 sub-tile (w & 1, w >> 1); lane l of a wave holds row
@@ -73,6 +74,55 @@ def test_old_clamp_let_other_waves_store_the_last_row(M):
     waves = {w for who in last for w, _, _ in who}
     assert any(len(who) > 1 for who in last)
     assert {w & 1 for w in waves} == {0, 1}
+
+
+def transposed_pieces(m0, n0, nc):
+    """Without a residual each wave writes its pieces into 8 KB of LDS, 64
+    rows of 8 sixteen-byte chunks at a time (chunk c of row r at slot
+    8 r + (c ^ (r mod 8))), and reads back slot-wise so that lane l of read
+    s holds row s * 8 + l // 8, chunk l % 8: 8 lanes per 128-byte row.
+    Returns (row, first column) stored per (wave, half, read, lane), after
+    checking that each read gets the piece of the row and chunk it stores."""
+    out = []
+    for w in range(8):
+        wm, wn = w & 1, w >> 1
+        for h in range(2):
+            slots = {}
+            for ii in range(2):
+                for j in range(2):
+                    for gp in range(2):
+                        for lane in range(64):
+                            r = ii * 32 + lane % 32          # row within the half
+                            c8 = j * 4 + gp * 2 + lane // 32  # piece column / 8
+                            slot = r * 8 + (c8 ^ (r & 7))
+                            assert slot not in slots
+                            # the piece's true place in the MFMA layout
+                            slots[slot] = (wm * 128 + (h * 2 + ii) * 32 + lane % 32,
+                                           wn * 64 + j * 32 + gp * 16 + (lane // 32) * 8)
+            assert sorted(slots) == list(range(512))
+            for sread in range(8):
+                for lane in range(64):
+                    r = sread * 8 + lane // 8
+                    c8 = lane % 8
+                    row, col = wm * 128 + h * 64 + r, wn * 64 + c8 * 8
+                    assert slots[r * 8 + (c8 ^ (r & 7))] == (row, col)
+                    out.append((m0 + row, n0 + col, ((row * nc) + col) * 2))
+    return out
+
+
+@pytest.mark.parametrize("M", [15, 300, 55093 - 49152])
+def test_transposed_stores_cover_each_valid_piece_once(M):
+    nc = 512
+    hits = {}
+    for m0 in range(0, M, BM):
+        for n0 in range(0, nc, BN):
+            tile_bytes = (min(M - m0, BM) * nc - n0) * 2
+            for row, col, off in transposed_pieces(m0, n0, nc):
+                if off + 16 > tile_bytes:
+                    assert row >= M
+                    continue
+                hits[(row, col)] = hits.get((row, col), 0) + 1
+    assert hits == {(r, c): 1 for r in range(M) for c in range(0, nc, 8)}
 
 
 def test_tile_bytes_fit_the_32_bit_resource():
