@@ -456,8 +456,11 @@ def main():
                                              case.heads, out=o.view(-1, t, d), workspace=ws,
                                              stream=stream, kernel_events=kev)
             else:
+                # a stack of layers over one batch builds the attention's
+                # work-unit table once, in its first layer
                 gsattn.block_mhsa_fwd(cur, cu, wqkv, wo, case.block_frames, case.heads, out=o,
-                                      workspace=ws, stream=stream, kernel_events=kev)
+                                      workspace=ws, stream=stream, kernel_events=kev,
+                                      reuse_unit_table=l > 0)
             cur = o
         return cur
 

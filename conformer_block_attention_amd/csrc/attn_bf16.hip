@@ -831,19 +831,30 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   stream_barrier();
   const int nflag = flist[0];
   if (nflag == 0) return;
+  // Each flagged item's bit is cleared again once it is recomputed, so every
+  // launch starts with clear flag words even when it reuses the unit table of
+  // an earlier launch (only this workgroup touches the bits of its items;
+  // other heads of a unit are other bits).
   if (nflag <= ATT_FLIST) {
     for (int i = 0; i < nflag; ++i) {
       const int v = flist[1 + i];
       const int u = v / heads;
       exact_item(qkv, table[1 + u], v - u * heads, d, scale_log2, O, wave, ATT_PRODUCER, pbuf[wave]);
     }
+    if ((int)threadIdx.x < nflag) {
+      const int v = flist[1 + threadIdx.x];
+      const int u = v / heads;
+      atomicAnd(&ovf[u], ~(1ull << (v - u * heads)));
+    }
   } else {  // more than the list holds: check every item of this workgroup
     Cursor c;
     c.r = 0;
     for (cursor_load(c, table, items, heads); c.valid; ++c.r, cursor_load(c, table, items, heads)) {
       const int u = c.v / heads;
-      if ((__atomic_load_n(&ovf[u], __ATOMIC_RELAXED) >> c.h) & 1)
+      if ((__atomic_load_n(&ovf[u], __ATOMIC_RELAXED) >> c.h) & 1) {
         exact_item(qkv, table[1 + u], c.h, d, scale_log2, O, wave, ATT_PRODUCER, pbuf[wave]);
+        if (threadIdx.x == 0) atomicAnd(&ovf[u], ~(1ull << c.h));
+      }
     }
   }
 }
@@ -852,8 +863,12 @@ static int g_num_cus = 0;
 
 int attn_bf16_table_entries(long long N) { return (int)(N + 1); }
 
+// build_table = false: `table` already holds the unit table of these spans
+// (from an earlier launch), and its flag words are clear (every launch clears
+// the bits it sets).
 hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long N, int d,
-                                  int heads, int B, void* o, void* table, hipStream_t stream) {
+                                  int heads, int B, void* o, void* table, hipStream_t stream,
+                                  bool build_table) {
   if (g_num_cus == 0) {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -864,10 +879,12 @@ hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long
   // workspace: the unit table, then (256-byte aligned) one flag word per unit
   unsigned long long* ovf =
       (unsigned long long*)((char*)table + ((16 * (N + 1) + 255) / 256) * 256);
-  build_unit_table_kernel<ATT_QG, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(sp, S, B, (int4*)table,
-                                                                                     ovf);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (build_table) {
+    build_unit_table_kernel<ATT_QG, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(sp, S, B,
+                                                                               (int4*)table, ovf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const long long units = attn_unit_bound(N, S, B, ATT_QG);
   const long long items = units * heads;
   const int grid = items < g_num_cus ? (int)items : g_num_cus;

@@ -21,7 +21,8 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int 
 hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
                                 int d, hipStream_t stream);
 hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long N, int d,
-                                  int heads, int B, void* o, void* table, hipStream_t stream);
+                                  int heads, int B, void* o, void* table, hipStream_t stream,
+                                  bool build_table = true);
 hipError_t launch_qkv_proj_f32(const void* x, const void* wqkv, void* qkv, int M, int d,
                                hipStream_t stream);
 hipError_t launch_bpe_pool_ctc(const void* logits, long long ld, const float* blank_prob,
@@ -253,9 +254,10 @@ gs_status debug_check_lengths(const int32_t* len, int32_t S, int32_t T, int* dfl
 // The attention step over sequences given as spans (packed or padded).
 gs_status attn_spans(const void* qkv, gs::SeqSpans sp, int32_t S, int64_t N, int32_t d,
                      int32_t heads, int32_t B, gs_dtype dtype, void* o, void* table,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool build_table = true) {
   hipError_t e = dtype == GS_BF16
-                     ? gs::launch_block_attn_bf16(qkv, sp, S, N, d, heads, B, o, table, stream)
+                     ? gs::launch_block_attn_bf16(qkv, sp, S, N, d, heads, B, o, table, stream,
+                                                  build_table)
                      : gs::launch_block_attn_f32(qkv, sp, S, N, d, heads, B, o, stream);
   return hip_status(e, "block_attn launch");
 }
@@ -439,11 +441,15 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
   if (p.N == 0) return GS_OK;
   GS_TRY(debug_check_cu(cu_seqlens, desc->num_seqs, p.N, p.dflag, stream));
 
+  if (desc->flags & ~GS_FWD_REUSE_UNIT_TABLE)
+    return fail(GS_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", desc->flags);
+  const bool build_table = !(desc->flags & GS_FWD_REUSE_UNIT_TABLE);
+
   GS_TRY(record(desc, 0, stream));
   GS_TRY(gs_qkv_proj(x, Wqkv, p.qkv, p.N, p.d, desc->dtype, stream));
   GS_TRY(record(desc, 1, stream));
-  GS_TRY(gs_block_attn(p.qkv, cu_seqlens, desc->num_seqs, p.N, p.d, heads, block_frames,
-                       desc->dtype, p.o, p.table, p.table_bytes, stream));
+  GS_TRY(attn_spans(p.qkv, gs::SeqSpans{cu_seqlens, 0}, desc->num_seqs, p.N, p.d, heads,
+                    block_frames, desc->dtype, p.o, p.table, stream, build_table));
   GS_TRY(record(desc, 2, stream));
   GS_TRY(gs_out_proj_residual(p.o, Wo, x, out, p.N, p.d, desc->dtype, stream));
   GS_TRY(record(desc, 3, stream));
@@ -465,7 +471,7 @@ gs_status gs_block_mhsa_fwd_noalloc(const void* x, const int32_t* cu_seqlens, co
   void* ws = nullptr;
   GS_TRY(scratch_of_current_device(&ws));
   const gs_mhsa_desc desc{num_seqs, total_frames, d_model, dtype, ws, GS_NOALLOC_SCRATCH_BYTES,
-                          nullptr};
+                          nullptr, 0u};
   return gs_block_mhsa_fwd(x, cu_seqlens, Wqkv, Wo, block_frames, heads, out, stream, &desc);
 }
 

@@ -47,7 +47,11 @@ class _Desc(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("kernel_events", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
     ]
+
+
+GS_FWD_REUSE_UNIT_TABLE = 1
 
 
 class _XattnDesc(ctypes.Structure):
@@ -162,8 +166,12 @@ def alloc_workspace(total_frames: int, d_model: int, dtype: torch.dtype, device=
 def block_mhsa_fwd(x: torch.Tensor, cu_seqlens: torch.Tensor, wqkv: torch.Tensor, wo: torch.Tensor,
                    block_frames: int, heads: int, out: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None,
-                   kernel_events: Optional["HipEvents"] = None) -> torch.Tensor:
-    """out = x + BlockMHSA(x), enqueued on `stream` (default: torch's current stream)."""
+                   kernel_events: Optional["HipEvents"] = None,
+                   reuse_unit_table: bool = False) -> torch.Tensor:
+    """out = x + BlockMHSA(x), enqueued on `stream` (default: torch's current stream).
+    reuse_unit_table: the workspace holds the attention work-unit table of an
+    earlier call with the same cu_seqlens, sizes and block length (e.g. the
+    previous layer of a stack), which is then not rebuilt."""
     lib = load()
     n, d = x.shape
     dt = _gs_dtype(x.dtype)
@@ -174,7 +182,8 @@ def block_mhsa_fwd(x: torch.Tensor, cu_seqlens: torch.Tensor, wqkv: torch.Tensor
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     desc = _Desc(int(cu_seqlens.numel()) - 1, int(n), int(d), dt, workspace.data_ptr(),
-                 int(workspace.numel()), kernel_events.handle_array() if kernel_events else None)
+                 int(workspace.numel()), kernel_events.handle_array() if kernel_events else None,
+                 GS_FWD_REUSE_UNIT_TABLE if reuse_unit_table else 0)
     _check(lib.gs_block_mhsa_fwd(
         _dev(x, "x"), _dev(cu_seqlens, "cu_seqlens"), _dev(wqkv, "Wqkv", x.dtype),
         _dev(wo, "Wo", x.dtype), int(block_frames), int(heads), _dev(out, "out", x.dtype),

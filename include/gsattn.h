@@ -78,7 +78,17 @@ typedef struct {
      before the projection kernel, after it, after the attention kernel and
      after the output-projection kernel, for per-kernel timing. */
   hipEvent_t* kernel_events;
+  /* 0, or GS_FWD_REUSE_UNIT_TABLE (gs_block_mhsa_fwd only, bf16): the
+     workspace already holds the attention work-unit table that an earlier
+     call on this stream built from the same cu_seqlens values, num_seqs,
+     total_frames, d_model, heads and block_frames, with this workspace, and
+     nothing has written the workspace since except such calls (a stack of
+     layers over one packed batch); the table is then not rebuilt.  With
+     anything else in the workspace the result is undefined. */
+  uint32_t flags;
 } gs_mhsa_desc;
+
+#define GS_FWD_REUSE_UNIT_TABLE 1u
 
 /* Bytes of workspace gs_block_mhsa_fwd needs for these sizes (0 on bad input). */
 size_t gs_block_mhsa_workspace_bytes(int64_t total_frames, int32_t d_model, gs_dtype dtype);

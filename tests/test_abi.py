@@ -91,6 +91,13 @@ def test_argument_errors(lib, kw, desc_kw, code):
     assert detail
 
 
+def test_unknown_desc_flags_are_rejected(lib):
+    desc = _desc()
+    desc.flags = 0x4
+    st, detail = _fwd(lib, desc)
+    assert st == gsattn.GS_ERR_INVALID_ARGUMENT and "flags" in detail
+
+
 def test_empty_input_is_noop(lib):
     # N = 0 returns before touching any pointer or the device
     st, _ = _fwd(lib, _desc(N=0, ws=None, wsb=0), x=None, wqkv=None, wo=None, out=None)

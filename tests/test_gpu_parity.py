@@ -232,8 +232,18 @@ def test_stage_block_attn_many_overflowed_items(orc):
     # about items / 256 per workgroup: all flagged where the heads are 1 and 2,
     # half where they are 0 and 3
     assert 65 * 256 < items < 2 * 64 * 256
-    o = gsattn.block_attn(qkv_cpu.to(G.dev()), torch.from_numpy(cu).to(G.dev()), H, B)
+    lib = gsattn.load()
+    ws = torch.full((int(lib.gs_block_attn_workspace_bytes(n)),), 0xFF, dtype=torch.uint8,
+                    device=G.dev())
+    o = gsattn.block_attn(qkv_cpu.to(G.dev()), torch.from_numpy(cu).to(G.dev()), H, B,
+                          workspace=ws)
     torch.cuda.synchronize()
+    # the flag words (after the 256-byte aligned unit table) are clear again:
+    # every recomputed item's bit is reset by the workgroup that set it
+    units = items // H
+    t_bytes = (16 * (n + 1) + 255) // 256 * 256
+    flags = ws[t_bytes:t_bytes + 8 * units].cpu()
+    assert int(flags.count_nonzero()) == 0
     got = o.double().cpu().numpy()
     assert np.all(np.isfinite(got))
     ref = orc.block_attn(qkv_cpu, cu, H, B)
@@ -551,6 +561,27 @@ def test_workload_chain16_full_layer(orc, layer):
     wqkv, wo = case.weights[layer]
     out = G.run(cur, cu, wqkv.to(G.dev()), wo.to(G.dev()), case.block_frames, case.heads)
     _chain_layer_check(orc, case, layer, cur, out, np.ones(case.n_frames, np.uint8), full=True)
+
+
+def test_chain_reuses_the_unit_table():
+    """Four layers of the headline chain with the work-unit table built once
+    (GS_FWD_REUSE_UNIT_TABLE from layer 2 on) give the bits of rebuilding it
+    every layer."""
+    G.print_case("chain unit-table reuse")
+    case = workloads.build_case(workloads.WORKLOADS["bf16_b128_chain16"])
+    cu = torch.from_numpy(case.cu).to(G.dev())
+    n, d = case.x.shape
+    outs = {}
+    for reuse in (False, True):
+        ws = gsattn.alloc_workspace(n, d, torch.bfloat16, G.dev())
+        cur = case.x.to(G.dev())
+        for layer, (wqkv, wo) in enumerate(case.weights[:4]):
+            cur = gsattn.block_mhsa_fwd(cur, cu, wqkv.to(G.dev()), wo.to(G.dev()),
+                                        case.block_frames, case.heads, workspace=ws,
+                                        reuse_unit_table=reuse and layer > 0)
+        torch.cuda.synchronize()
+        outs[reuse] = cur
+    assert torch.equal(outs[False], outs[True])
 
 
 def test_chain16_free_running(orc):
