@@ -3,9 +3,11 @@
 One step = one call of gs_block_mhsa_fwd (Q|K|V projection, block attention,
 output projection with residual) over the whole packed batch, inputs already
 resident in HBM.  Prints one JSON line.  The step time is the median over the
-timed steps of the GPU time from a step's first kernel to its last (HIP
-events the library records on the launch stream), with p10, p90, the mean
-and the wall-clock mean beside it; per-kernel times are means.
+timed steps of the GPU time between HIP events recorded on the launch stream
+at the step boundaries (K steps back to back, no events between a step's
+kernels), with p10, p90, the mean and the wall-clock mean beside it.
+Per-kernel times are means over a second pass of K steps in which the
+library records events between the stages.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
   python bench.py --copy-calibration MB   (plain device copy of MB MiB, for
@@ -156,6 +158,23 @@ def cpu_baseline_xattn(c, budget_s: float = 12.0):
                                         f"{el:.1f} s"}
 
 
+def time_steps(step, steps: int, stream):
+    """GPU milliseconds of each of `steps` calls of step() run back to back,
+    from HIP events recorded on `stream` at the step boundaries only (an
+    event between two kernels leaves the GPU idle for about 6 us on this
+    chip, which no caller pays), and the wall-clock seconds of the run."""
+    bev = gsattn.HipEvents(steps + 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    bev.record(0, stream)
+    for k in range(steps):
+        step()
+        bev.record(k + 1, stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    return np.array([bev.elapsed_ms(k, k + 1) for k in range(steps)]), el
+
+
 def bench_xattn(args):
     """The window cross-attention of the Q-Former projector on its workload."""
     w = workloads.XATTN_WORKLOADS[args.workload]
@@ -180,13 +199,13 @@ def bench_xattn(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    step_ms, el = time_steps(step, args.steps, stream)
+    # per-kernel durations: a second pass with the library's stage events
     ev = gsattn.HipEvents(4 * args.steps)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for k in range(args.steps):
         step(ev, 4 * k)
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
     names = ("kv_q_proj", "window_attn", "out_proj")
     avg = {k: float(np.mean([ev.elapsed_ms(4 * i + j, 4 * i + j + 1) for i in range(args.steps)]))
            for j, k in enumerate(names)}
@@ -209,12 +228,16 @@ def bench_xattn(args):
     roof["kernel"] = dom
     roof["traffic"] = None
     total = sum(fl.values())
-    sec = el / args.steps
+    p10, p50, p90 = (float(v) for v in np.percentile(step_ms, [10, 50, 90]))
+    sec = p50 * 1e-3
     rec = {
         "metric": f"encoder frames/sec through the window cross-attention ({w.name}); "
                   f"% of matrix peak",
         "value": n / sec, "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": sec * 1e3,
+        "step_ms": {"median": p50, "p10": p10, "p90": p90, "mean": float(np.mean(step_ms)),
+                    "wall_mean": el / args.steps * 1e3},
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "global_batch": int(len(c.lengths)), "frames": int(n),
                    "windows": int(nw), "queries": nq, "feat_dim": int(f), "d_q": int(dq),
@@ -255,15 +278,8 @@ def bench_ctc(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    step_ms, el = time_steps(step, args.steps, torch.cuda.current_stream())
+    p10, ms, p90 = (float(v) for v in np.percentile(step_ms, [10, 50, 90]))
     by = 2 * n * ld + 4 * n + 8 * npos + 4 * len(lengths)  # logits, blank probs, outputs
     gbs = by / (ms * 1e-3) / 1e9
     cpu = None
@@ -287,7 +303,9 @@ def bench_ctc(args):
         "metric": f"encoder frames/sec through BPE pooling + CTC greedy decoding ({CTC_WORKLOAD}); "
                   f"% of HBM peak",
         "value": n / (ms * 1e-3), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "wall_ms_per_step": el / args.steps * 1e3,
+        "warmup": args.warmup, "ms_per_step": ms,
+        "step_ms": {"median": ms, "p10": p10, "p90": p90, "mean": float(np.mean(step_ms)),
+                    "wall_mean": el / args.steps * 1e3},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": CTC_WORKLOAD, "global_batch": int(len(lengths)), "frames": int(n),
@@ -468,13 +486,16 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # step timing: K steps back to back, events at the step boundaries only
+    step_ms, el = time_steps(step, args.steps, stream)
+
+    # Kernel timing: K more steps with the library's events between the
+    # stages, for the per-kernel durations.
     ev = gsattn.HipEvents(4 * nl * args.steps)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for k in range(args.steps):
         step(ev, 4 * nl * k)
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
 
     per = {k: [] for k in KERNELS}
     for i in range(nl * args.steps):
@@ -483,10 +504,6 @@ def main():
         per["block_attn"].append(ev.elapsed_ms(b + 1, b + 2))
         per["out_proj"].append(ev.elapsed_ms(b + 2, b + 3))
     avg_ms = {k: float(np.mean(v)) for k, v in per.items()}
-    # one step on the GPU: from the first kernel of its first layer to the end
-    # of the last kernel of its last layer
-    step_ms = np.array([ev.elapsed_ms(4 * nl * k, 4 * nl * k + 4 * (nl - 1) + 3)
-                        for k in range(args.steps)])
     p10, p50, p90 = (float(v) for v in np.percentile(step_ms, [10, 50, 90]))
 
     ms_step = p50

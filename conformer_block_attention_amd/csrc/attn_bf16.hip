@@ -859,9 +859,24 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
   }
 }
 
+// The unit table as a kernel of its own (one workgroup).
+__global__ __launch_bounds__(1024) void build_unit_table_kernel(UnitTableJob j) {
+  __shared__ int lds[UNIT_TABLE_LDS_INTS];
+  build_unit_table(j, lds);
+}
+
 static int g_num_cus = 0;
 
 int attn_bf16_table_entries(long long N) { return (int)(N + 1); }
+
+// The unit-table build of a launch over these spans, for another launch to
+// run in a spare workgroup (the table in the workspace `table`, then,
+// 256-byte aligned, one overflow flag word per unit).
+UnitTableJob attn_bf16_table_job(SeqSpans sp, int S, long long N, int B, void* table) {
+  unsigned long long* ovf =
+      (unsigned long long*)((char*)table + ((16 * (N + 1) + 255) / 256) * 256);
+  return UnitTableJob{sp, S, B, ATT_QG, ATT_KC, (int4*)table, ovf};
+}
 
 // build_table = false: `table` already holds the unit table of these spans
 // (from an earlier launch), and its flag words are clear (every launch clears
@@ -876,12 +891,10 @@ hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long
       n = 256;
     g_num_cus = n;
   }
-  // workspace: the unit table, then (256-byte aligned) one flag word per unit
-  unsigned long long* ovf =
-      (unsigned long long*)((char*)table + ((16 * (N + 1) + 255) / 256) * 256);
+  const UnitTableJob job = attn_bf16_table_job(sp, S, N, B, table);
+  unsigned long long* ovf = job.flags;
   if (build_table) {
-    build_unit_table_kernel<ATT_QG, ATT_KC><<<dim3(1), dim3(1024), 0, stream>>>(sp, S, B,
-                                                                               (int4*)table, ovf);
+    hipLaunchKernelGGL(build_unit_table_kernel, dim3(1), dim3(1024), 0, stream, job);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

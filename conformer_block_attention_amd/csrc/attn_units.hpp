@@ -87,70 +87,92 @@ __device__ bool find_unit(SeqSpans sp, int S, int B, int u, AttnUnit& out) {
 // table[0] = {number of units, 0, 0, 0};
 // table[1 + i] = {row0, L, q0, qn} of the i-th
 // unit in order of decreasing cost, the cost being the number of key chunks
-// of KC keys a unit takes, ceil(L/KC) (capped at 1023; the order of units of
+// of kc keys a unit takes, ceil(L/kc) (capped at 1023; the order of units of
 // equal cost is unspecified).  With the costliest units first, a
 // persistent kernel that deals them out in a snake order (round r hands
 // position r*G + w to workgroup w for even r, to G-1-w for odd r) keeps its
 // workgroups within about one unit of each other.
 // Every unit holds at least one row, so N + 1 entries always suffice.  If
 // `flags` is not null, flags[i] is cleared for every unit i.
-// One workgroup; a counting sort over the cost: a histogram pass and a
-// placement pass over the sequences, 1024 sequences at a time.
-template <int QG, int KC>
-__global__ __launch_bounds__(1024) void build_unit_table_kernel(SeqSpans sp, int S, int B,
-                                                               int4* __restrict__ table,
-                                                               unsigned long long* __restrict__ flags) {
-  constexpr int BINS = 1024;
-  __shared__ int next[BINS];  // per cost bin: count, then next free position
-  __shared__ int scan[BINS];
-  const int tid = threadIdx.x;
-  const int upb = (B - 1) / QG + 1;
-  next[tid] = 0;
+struct UnitTableJob {
+  SeqSpans sp;
+  int S, B;
+  int qg, kc;                       // query rows per unit, keys per chunk
+  int4* table;                      // null: nothing to build
+  unsigned long long* flags;
+};
+
+constexpr int UNIT_BINS = 1024;
+constexpr int UNIT_TABLE_LDS_INTS = UNIT_BINS + 16;
+
+// A counting sort over the cost, by one workgroup (blockDim.x a multiple of
+// 64 that divides 1024; every thread calls it): a count pass and a
+// placement pass over the sequences, blockDim.x sequences at a time.  The
+// units of a sequence come in two runs of equal cost (those of its full
+// blocks, those of its last block), each counted and placed with one LDS
+// atomic.  lds: UNIT_TABLE_LDS_INTS ints.
+__device__ inline void build_unit_table(const UnitTableJob& j, int* lds) {
+  int* next = lds;                  // per cost bin: count, then next free position
+  int* wsum = lds + UNIT_BINS;      // per wave: the count of its threads' bins
+  const int T = blockDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = UNIT_BINS / T;    // bins per thread in the scan
+  const int upb = (j.B - 1) / j.qg + 1;
+  auto bin_of = [&](int L) {  // bin 0 holds the costliest units
+    const int cost = (L + j.kc - 1) / j.kc;
+    return UNIT_BINS - 1 - min(cost, UNIT_BINS - 1);
+  };
+  auto put = [&](int pos, int row0, int L, int g) {
+    j.table[1 + pos] = make_int4(row0, L, g * j.qg, min(j.qg, L - g * j.qg));
+    if (j.flags) j.flags[pos] = 0;
+  };
+  for (int b = tid; b < UNIT_BINS; b += T) next[b] = 0;
   __syncthreads();
-  // the v-th unit of a sequence of `len` rows starting at `start`
-  auto unit = [&](int start, int len, int v) {
-    const int nb = (len - 1) / B + 1;
-    int j = v / upb;
-    if (j > nb - 1) j = nb - 1;
-    const int g = v - j * upb;
-    const int L = (j < nb - 1) ? B : len - (nb - 1) * B;
-    return make_int4(start + j * B, L, g * QG, min(QG, L - g * QG));
-  };
-  auto bin_of = [&](int4 e) {  // bin 0 holds the costliest units
-    const int cost = (e.y + KC - 1) / KC;
-    return BINS - 1 - min(cost, BINS - 1);
-  };
   for (int pass = 0; pass < 2; ++pass) {
-    for (int c0 = 0; c0 < S; c0 += 1024) {
+    for (int c0 = 0; c0 < j.S; c0 += T) {
       const int s = c0 + tid;
-      int len = 0;
-      if (s < S) len = sp.len(s);
-      const int n = units_of_seq<QG>(len, B, upb);
-      if (n > 0) {
-        const int start = sp.start(s);
-        for (int v = 0; v < n; ++v) {
-          const int4 e = unit(start, len, v);
-          const int pos = atomicAdd(&next[bin_of(e)], 1);
-          if (pass == 1) {
-            table[1 + pos] = e;
-            if (flags) flags[pos] = 0;
+      const int len = s < j.S ? j.sp.len(s) : 0;
+      if (len > 0) {
+        const int nb = (len - 1) / j.B + 1;
+        const int tail = len - (nb - 1) * j.B;
+        const int nfull = (nb - 1) * upb;      // units of the full blocks
+        const int ntail = (tail - 1) / j.qg + 1;  // units of the last block
+        if (pass == 0) {
+          if (nfull) atomicAdd(&next[bin_of(j.B)], nfull);
+          atomicAdd(&next[bin_of(tail)], ntail);
+        } else {
+          const int start = j.sp.start(s);
+          if (nfull) {
+            const int pos = atomicAdd(&next[bin_of(j.B)], nfull);
+            for (int v = 0; v < nfull; ++v) {
+              const int blk = v / upb;
+              put(pos + v, start + blk * j.B, j.B, v - blk * upb);
+            }
           }
+          const int pos = atomicAdd(&next[bin_of(tail)], ntail);
+          for (int g = 0; g < ntail; ++g) put(pos + g, start + (nb - 1) * j.B, tail, g);
         }
       }
     }
     __syncthreads();
     if (pass == 0) {  // counts -> first position of each bin (exclusive scan)
-      const int n = next[tid];
-      scan[tid] = n;
-      __syncthreads();
-      for (int off = 1; off < BINS; off <<= 1) {  // inclusive Hillis-Steele scan
-        const int y = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += y;
-        __syncthreads();
+      int sum = 0;
+      for (int i = 0; i < per; ++i) sum += next[tid * per + i];
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
       }
-      next[tid] = scan[tid] - n;
-      if (tid == 0) table[0] = make_int4(scan[BINS - 1], 0, 0, 0);
+      if (lane == 63) wsum[wave] = incl;
+      __syncthreads();
+      int run = incl - sum;
+      for (int w = 0; w < wave; ++w) run += wsum[w];
+      for (int i = 0; i < per; ++i) {
+        const int c = next[tid * per + i];
+        next[tid * per + i] = run;
+        run += c;
+      }
+      if (tid == T - 1) j.table[0] = make_int4(run, 0, 0, 0);
       __syncthreads();
     }
   }

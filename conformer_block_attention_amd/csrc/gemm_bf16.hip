@@ -39,6 +39,7 @@
 //     row M of the tile, so the hardware drops the stores of rows >= M and
 //     their residual reads return zero (a stored copy of row M-1 would race
 //     with C == R in place).  Requires K % BK == 0 and Nc % BN == 0.
+#include "attn_units.hpp"
 #include "gs_device.hpp"
 
 namespace gs {
@@ -143,7 +144,7 @@ __device__ __forceinline__ void swap_lo_hi(unsigned& x, unsigned& y) {
 template <int BM, int BN, int BK, int NST, bool DEFER, int EARLY, int SPLIT, bool RESID>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* R, bf16* C,
-    int M, int Nc, int K) {
+    int M, int Nc, int K, UnitTableJob job) {
   using G = TileGeom<BK>;
   using CopyA = TileCopy<BM, BK, true>;        // activation rows: the last panel is ragged
   using CopyB = TileCopy<BN, BK, false>;       // weight rows: Nc % BN == 0
@@ -162,6 +163,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   static_assert(KK % 2 == 0, "register double buffer assumes an even chunk count");
   static_assert((NOUT - EARLY) % SPLIT == 0, "stores spread evenly over the early steps");
   __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STAGE];
+  static_assert(NST * STAGE * 2 >= UNIT_TABLE_LDS_INTS * 4, "LDS for the side job");
+
+  // With a job, the grid's last workgroup builds the attention's work-unit
+  // table instead of taking tiles (a launch of fewer tiles than CUs runs it
+  // on a CU that would otherwise idle).
+  if (job.table && blockIdx.x == gridDim.x - 1) {
+    build_unit_table(job, (int*)smem);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
 
   // ---- tile order ----
   // k-th tile of this workgroup as (panel, column tile), or panel = -1.
-  const int Gs = gridDim.x;
+  const int Gs = gridDim.x - (job.table ? 1 : 0);
   // (else: plain round-robin over tiles)
   const bool by_xcd = (Gs & 7) == 0 && mt_count >= 8 && (long long)mt_count * nt_count > Gs;
   const int xcd = blockIdx.x & 7;
@@ -506,18 +516,22 @@ static int gemm_persistent_grid(int tiles) {
 }
 
 hipError_t launch_qkv_proj_bf16_pp(const void* x, const void* wqkv, void* qkv, int M, int d,
-                                   hipStream_t stream);
+                                   hipStream_t stream, const UnitTableJob* job, bool* job_done);
 
+// job (optional): a unit-table build to run in a spare workgroup of the
+// launch; *job_done tells whether it was enqueued (else the caller runs it).
 hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int M, int d,
-                                hipStream_t stream) {
+                                hipStream_t stream, const UnitTableJob* job, bool* job_done) {
+  if (job_done) *job_done = false;
   // 3d is a multiple of 256 when d is (two waves per SIMD, 256 x 256 tiles);
   // otherwise 3d = 384 * (d / 128) is a multiple of 192
-  if ((3 * d) % 256 == 0) return launch_qkv_proj_bf16_pp(x, wqkv, qkv, M, d, stream);
+  if ((3 * d) % 256 == 0)
+    return launch_qkv_proj_bf16_pp(x, wqkv, qkv, M, d, stream, job, job_done);
   const int Nc = 3 * d;
   const int mt = (M + GEMM_BM - 1) / GEMM_BM;
   hipLaunchKernelGGL((gemm_bf16_nt_kernel<GEMM_BM, 192, 64, 2, false, 0, 12, false>), dim3(gemm_persistent_grid(mt * (Nc / 192))),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)x, (const bf16*)wqkv,
-                     (const bf16*)nullptr, (bf16*)qkv, M, Nc, d);
+                     (const bf16*)nullptr, (bf16*)qkv, M, Nc, d, UnitTableJob{});
   return hipGetLastError();
 }
 
@@ -530,7 +544,7 @@ hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, vo
   const int mt = (M + GEMM_BM - 1) / GEMM_BM;
   hipLaunchKernelGGL((gemm_bf16_nt_kernel<GEMM_BM, 128, 64, 3, false, 0, 8, true>), dim3(gemm_persistent_grid(mt * (d / 128))),
                      dim3(GEMM_THREADS), 0, stream, (const bf16*)o, (const bf16*)wo,
-                     (const bf16*)x, (bf16*)out, M, d, d);
+                     (const bf16*)x, (bf16*)out, M, d, d, UnitTableJob{});
   return hipGetLastError();
 }
 
@@ -550,26 +564,29 @@ int gemm_tail_tile_rows(int rows, int Nc) {
 
 template <int BM, bool RESID>
 static void launch_tail(const bf16* A, const bf16* W, const bf16* R, bf16* C, int rows, int Nc,
-                        int K, hipStream_t stream) {
+                        int K, hipStream_t stream, const UnitTableJob* job) {
   const int tiles = (rows + BM - 1) / BM * (Nc / 128);
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, 128, 64, 3, false, 0, 4, RESID>), dim3(tiles),
-                     dim3(GEMM_THREADS), 0, stream, A, W, R, C, rows, Nc, K);
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, 128, 64, 3, false, 0, 4, RESID>),
+                     dim3(tiles + (job ? 1 : 0)), dim3(GEMM_THREADS), 0, stream, A, W, R, C, rows,
+                     Nc, K, job ? *job : UnitTableJob{});
 }
 
-// bm: gemm_tail_tile_rows(rows, Nc); requires K % 64 == 0.
+// bm: gemm_tail_tile_rows(rows, Nc); requires K % 64 == 0.  job (optional):
+// a unit-table build for one more workgroup of the launch.
 hipError_t launch_gemm_tail_bf16(const void* A, const void* W, const void* R, void* C, int rows,
-                                 int Nc, int K, int bm, hipStream_t stream) {
+                                 int Nc, int K, int bm, hipStream_t stream,
+                                 const UnitTableJob* job) {
   const bf16 *a = (const bf16*)A, *w = (const bf16*)W, *r = (const bf16*)R;
   bf16* c = (bf16*)C;
   switch (bm * 2 + (R != nullptr)) {
-    case 128: launch_tail<64, false>(a, w, r, c, rows, Nc, K, stream); break;
-    case 129: launch_tail<64, true>(a, w, r, c, rows, Nc, K, stream); break;
-    case 256: launch_tail<128, false>(a, w, r, c, rows, Nc, K, stream); break;
-    case 257: launch_tail<128, true>(a, w, r, c, rows, Nc, K, stream); break;
-    case 384: launch_tail<192, false>(a, w, r, c, rows, Nc, K, stream); break;
-    case 385: launch_tail<192, true>(a, w, r, c, rows, Nc, K, stream); break;
-    case 512: launch_tail<256, false>(a, w, r, c, rows, Nc, K, stream); break;
-    case 513: launch_tail<256, true>(a, w, r, c, rows, Nc, K, stream); break;
+    case 128: launch_tail<64, false>(a, w, r, c, rows, Nc, K, stream, job); break;
+    case 129: launch_tail<64, true>(a, w, r, c, rows, Nc, K, stream, job); break;
+    case 256: launch_tail<128, false>(a, w, r, c, rows, Nc, K, stream, job); break;
+    case 257: launch_tail<128, true>(a, w, r, c, rows, Nc, K, stream, job); break;
+    case 384: launch_tail<192, false>(a, w, r, c, rows, Nc, K, stream, job); break;
+    case 385: launch_tail<192, true>(a, w, r, c, rows, Nc, K, stream, job); break;
+    case 512: launch_tail<256, false>(a, w, r, c, rows, Nc, K, stream, job); break;
+    case 513: launch_tail<256, true>(a, w, r, c, rows, Nc, K, stream, job); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

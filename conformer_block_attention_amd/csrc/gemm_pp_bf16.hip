@@ -46,6 +46,7 @@
 //     row M-1 would race with C == R in place: another wave may already have
 //     written row M-1 when the copy reads its residual.)
 //     Requires K % 64 == 0 and Nc % BN == 0.
+#include "attn_units.hpp"
 #include "gs_device.hpp"
 
 namespace gs {
@@ -338,13 +339,15 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
               const int c8 = j * 4 + gp * 2 + half;
               xt[r * 8 + (c8 ^ (r & 7))] = u32x4_t{x0, x1, y0, y1};
             }
+        // one per-lane offset; the row step goes in the uniform soffset
+        const unsigned st_base =
+            (unsigned)((wm * 128 + (lane >> 3)) * Nc + wn * WN + (lane & 7) * 8) * 2u;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const int r = s * 8 + (lane >> 3);
           const int c8 = lane & 7;
           const u32x4_t v = xt[r * 8 + (c8 ^ (r & 7))];
-          __builtin_amdgcn_raw_buffer_store_b128(
-              v, out_rs, (unsigned)((wm * 128 + h * 64 + r) * Nc + wn * WN + c8 * 8) * 2u, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, out_rs, st_base, (h * 64 + s * 8) * Nc * 2, 0);
         }
       }
     } else
@@ -468,7 +471,8 @@ static int pp_persistent_grid(int tiles) {
 
 int gemm_tail_tile_rows(int rows, int Nc);
 hipError_t launch_gemm_tail_bf16(const void* A, const void* W, const void* R, void* C, int rows,
-                                 int Nc, int K, int bm, hipStream_t stream);
+                                 int Nc, int K, int bm, hipStream_t stream,
+                                 const UnitTableJob* job);
 
 // Load balance: 256 x 256 tiles over the CUs leave a partial last round,
 // which a few CUs would run while the others wait.  The panels (256-row
@@ -498,9 +502,12 @@ static int pp_split_rows(int M, int Nc, int* tail_bm) {
 }
 
 // m_dev (optional): the row count on the device, at most M; one launch then.
+// job (optional): a unit-table build, run by one more workgroup of the
+// small-tile launch if there is one (*job_done then set).
 template <bool RESID>
 static hipError_t pp_launch(const bf16* A, const bf16* W, const bf16* R, bf16* C, int M, int Nc,
-                            int K, hipStream_t stream, const int* m_dev = nullptr) {
+                            int K, hipStream_t stream, const int* m_dev = nullptr,
+                            const UnitTableJob* job = nullptr, bool* job_done = nullptr) {
   auto launch = [&](int rows, const int* md) {
     const int mt = (rows + pp::BM - 1) / pp::BM;
     hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, RESID, 2>),
@@ -517,15 +524,17 @@ static hipError_t pp_launch(const bf16* A, const bf16* W, const bf16* R, bf16* C
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || m1 == M) return e;
   const size_t a_off = (size_t)m1 * K, c_off = (size_t)m1 * Nc;
-  return launch_gemm_tail_bf16(A + a_off, W, RESID ? R + c_off : nullptr, C + c_off, M - m1, Nc,
-                               K, tail_bm, stream);
+  e = launch_gemm_tail_bf16(A + a_off, W, RESID ? R + c_off : nullptr, C + c_off, M - m1, Nc, K,
+                            tail_bm, stream, job);
+  if (e == hipSuccess && job && job_done) *job_done = true;
+  return e;
 }
 
 hipError_t launch_qkv_proj_bf16_pp(const void* x, const void* wqkv, void* qkv, int M, int d,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, const UnitTableJob* job, bool* job_done) {
   // 3d = 384 * heads is a multiple of 256 for an even head count
   return pp_launch<false>((const bf16*)x, (const bf16*)wqkv, nullptr, (bf16*)qkv, M, 3 * d, d,
-                          stream);
+                          stream, nullptr, job, job_done);
 }
 
 hipError_t launch_out_proj_bf16_pp(const void* o, const void* wo, const void* x, void* out, int M,

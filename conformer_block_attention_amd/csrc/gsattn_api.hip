@@ -17,7 +17,9 @@
 
 namespace gs {
 hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int M, int d,
-                                hipStream_t stream);
+                                hipStream_t stream, const UnitTableJob* job = nullptr,
+                                bool* job_done = nullptr);
+UnitTableJob attn_bf16_table_job(SeqSpans sp, int S, long long N, int B, void* table);
 hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
                                 int d, hipStream_t stream);
 hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long N, int d,
@@ -446,10 +448,23 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
   const bool build_table = !(desc->flags & GS_FWD_REUSE_UNIT_TABLE);
 
   GS_TRY(record(desc, 0, stream));
-  GS_TRY(gs_qkv_proj(x, Wqkv, p.qkv, p.N, p.d, desc->dtype, stream));
+  bool table_built = false;
+  if (desc->dtype == GS_BF16 && build_table) {
+    // the projection's small-tile launch, if it has one, builds the
+    // attention's unit table in a workgroup of its own
+    const gs::UnitTableJob job = gs::attn_bf16_table_job(gs::SeqSpans{cu_seqlens, 0},
+                                                         desc->num_seqs, p.N, block_frames,
+                                                         p.table);
+    GS_TRY(hip_status(gs::launch_qkv_proj_bf16(x, Wqkv, p.qkv, (int)p.N, p.d, stream, &job,
+                                               &table_built),
+                      "qkv_proj launch"));
+  } else {
+    GS_TRY(gs_qkv_proj(x, Wqkv, p.qkv, p.N, p.d, desc->dtype, stream));
+  }
   GS_TRY(record(desc, 1, stream));
   GS_TRY(attn_spans(p.qkv, gs::SeqSpans{cu_seqlens, 0}, desc->num_seqs, p.N, p.d, heads,
-                    block_frames, desc->dtype, p.o, p.table, stream, build_table));
+                    block_frames, desc->dtype, p.o, p.table, stream,
+                    build_table && !table_built));
   GS_TRY(record(desc, 2, stream));
   GS_TRY(gs_out_proj_residual(p.o, Wo, x, out, p.N, p.d, desc->dtype, stream));
   GS_TRY(record(desc, 3, stream));

@@ -352,6 +352,7 @@ class HipEvents:
                                                   ctypes.c_void_p]
         self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self._arr = (ctypes.c_void_p * count)()
         for i in range(count):
             h = ctypes.c_void_p()
@@ -371,6 +372,13 @@ class HipEvents:
         if offset + 4 > self.count:
             raise IndexError(offset)
         return _EventView(self, offset)
+
+    def record(self, i: int, stream=None) -> None:
+        """Record event i on `stream` (a torch stream, a raw handle, or None
+        for the null stream)."""
+        h = getattr(stream, "cuda_stream", stream) or 0
+        if self._hip.hipEventRecord(self._arr[i], ctypes.c_void_p(int(h))) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, i: int, j: int) -> float:
         """Milliseconds between events i and j (waits for j)."""
