@@ -246,9 +246,13 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 }
 #undef GS_VMCNT
 
-// Position in a workgroup's stream of stages.  Items are taken in snake
-// order over the cost-sorted unit table: round r gives this workgroup the
-// item at position r*G + w (even r) or r*G + G-1-w (odd r).
+// Position in a workgroup's stream of stages.  Items are dealt in snake
+// order over the cost-sorted unit table: round r gives workgroup w the item
+// at position r*G + w (even r) or r*G + G-1-w (odd r).  Workgroups in every
+// other group of 8 (w / 8 odd) run their items in the reverse order: each
+// workgroup keeps the same items and the same total, but half of them then
+// start with their cheapest items, so item ends (each workgroup stores 56 KB
+// of O there) do not fall on all CUs at once.
 struct Cursor {
   int r;       // round
   int v;       // work item (unit position * heads + head)
@@ -259,7 +263,15 @@ struct Cursor {
 };
 
 __device__ __forceinline__ void cursor_index(Cursor& c, int items) {
-  c.v = c.r * (int)gridDim.x + ((c.r & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x);
+  const int G = (int)gridDim.x, w = (int)blockIdx.x;
+  int r = c.r;
+  if ((w >> 3) & 1) {  // reversed: this workgroup's rounds counted from its last
+    const int rl = items / G;                          // the last, partial round
+    const int sl = (rl & 1) ? G - 1 - w : w;           // this workgroup's slot in it
+    const int R = rl + (rl * G + sl < items ? 1 : 0);  // this workgroup's item count
+    r = R - 1 - r;
+  }
+  c.v = r < 0 ? items : r * G + ((r & 1) ? G - 1 - w : w);
   c.valid = c.v < items;
   c.s = 0;
 }
