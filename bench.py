@@ -37,8 +37,8 @@ NOMINAL_CLOCK_MHZ = 2400.0  # the clock the published peaks are quoted at
 KERNELS = ("qkv_proj", "block_attn", "out_proj")
 HEADLINE_METRIC = "encoder frames/sec through block-MHSA (bf16, B=128 packed); % bf16 MFMA peak"
 KERNEL_SOURCES = {
-    "qkv_proj": ["gemm_bf16.hip", "gemm_pp_bf16.hip"],
-    "out_proj": ["gemm_bf16.hip", "gemm_pp_bf16.hip"],
+    "qkv_proj": ["gemm_bf16.hip", "gemm_pp_bf16.hip", "attn_units.hpp"],
+    "out_proj": ["gemm_bf16.hip", "gemm_pp_bf16.hip", "attn_units.hpp"],
     "block_attn": ["attn_bf16.hip", "attn_units.hpp"],
 }
 
