@@ -15,7 +15,7 @@
 // A workgroup is 7 math waves (32 query rows each) and one copy wave:
 //   * the copy wave streams the K|V rows of its items, 32 keys per stage,
 //     through an LDS ring of 8 stages of 16 KB with 16-byte global->LDS direct
-//     copies, 4 stages ahead and across item boundaries, and waits for each
+//     copies, 3 stages ahead and across item boundaries, and waits for each
 //     stage's copies before the stage's workgroup barrier; the math waves
 //     never issue ring copies (a copy issued behind a saturated memory pipe
 //     holds its wave for hundreds of cycles);
@@ -60,7 +60,7 @@ constexpr int ATT_KC = 32;           // keys per key chunk
 constexpr float ATT_HEADROOM = 32.f;  // log2 margin of a score over its row's reference
 constexpr int DH = 128;
 constexpr int ATT_NST = 8;           // ring stages
-constexpr int ATT_AHEAD = 4;         // copies run this many stages ahead (<= 63 in flight)
+constexpr int ATT_AHEAD = 3;         // copies run this many stages ahead (<= 63 in flight)
 constexpr int STAGE_ELEMS = 8192;    // 16 KB: 64 rows of 128 bf16
 constexpr int COPIES = 16;           // 1 KB wave copies per stage, all by the copy wave
 
@@ -248,11 +248,13 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 
 // Position in a workgroup's stream of stages.  Items are dealt in snake
 // order over the cost-sorted unit table: round r gives workgroup w the item
-// at position r*G + w (even r) or r*G + G-1-w (odd r).  Workgroups in every
-// other group of 8 (w / 8 odd) run their items in the reverse order: each
-// workgroup keeps the same items and the same total, but half of them then
-// start with their cheapest items, so item ends (each workgroup stores 56 KB
-// of O there) do not fall on all CUs at once.
+// at position r*G + w (even r) or r*G + G-1-w (odd r).  Odd workgroups run
+// their items in the reverse order: each workgroup keeps the same items and
+// the same total, but half of them then start with their cheapest items, so
+// item ends (each workgroup stores 56 KB of O there) do not fall on all CUs
+// at once.  Workgroups w and w + 8 sit on the same XCD and, in a round, run
+// the same head of consecutive units (the query groups of one long block
+// share its K|V in that XCD's L2); both run in the same direction.
 struct Cursor {
   int r;       // round
   int v;       // work item (unit position * heads + head)
@@ -265,7 +267,7 @@ struct Cursor {
 __device__ __forceinline__ void cursor_index(Cursor& c, int items) {
   const int G = (int)gridDim.x, w = (int)blockIdx.x;
   int r = c.r;
-  if ((w >> 3) & 1) {  // reversed: this workgroup's rounds counted from its last
+  if (w & 1) {  // reversed: this workgroup's rounds counted from its last
     const int rl = items / G;                          // the last, partial round
     const int sl = (rl & 1) ? G - 1 - w : w;           // this workgroup's slot in it
     const int R = rl + (rl * G + sl < items ? 1 : 0);  // this workgroup's item count

@@ -2,8 +2,8 @@
 to its persistent workgroups.
 
 Items are dealt in snake order over the cost-sorted unit table: round r gives
-workgroup w the item r*G + w (even r) or r*G + G-1-w (odd r).  Workgroups with
-w / 8 odd run their own items in the reverse order.  The model repeats the
+workgroup w the item r*G + w (even r) or r*G + G-1-w (odd r).  Odd workgroups
+run their own items in the reverse order.  The model repeats the
 kernel's cursor arithmetic (the round count R of a workgroup from the last,
 partial round) and checks that every item is run exactly once, that a
 reversed workgroup runs exactly the items of the forward deal, in reverse,
@@ -16,7 +16,7 @@ import pytest
 def item_at(r, w, G, items):
     """The kernel's cursor: the item of this workgroup's r-th step (or items
     when it has none)."""
-    if (w >> 3) & 1:
+    if w & 1:
         rl = items // G
         sl = G - 1 - w if rl & 1 else w
         R = rl + (1 if rl * G + sl < items else 0)
@@ -54,7 +54,7 @@ def test_every_item_once_and_reversed_groups(items, cus):
     seen = np.zeros(items, np.int32)
     for w in range(G):
         got, fwd = run_order(w, G, items), forward_items(w, G, items)
-        assert got == (fwd[::-1] if (w >> 3) & 1 else fwd)
+        assert got == (fwd[::-1] if w & 1 else fwd)
         for v in got:
             seen[v] += 1
     assert np.all(seen == 1)
