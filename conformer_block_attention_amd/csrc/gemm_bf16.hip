@@ -39,6 +39,11 @@
 //     row M of the tile, so the hardware drops the stores of rows >= M and
 //     their residual reads return zero (a stored copy of row M-1 would race
 //     with C == R in place).  Requires K % BK == 0 and Nc % BN == 0.
+//   * side job: a launch of fewer tiles than CUs (the round of small tiles
+//     after the two-wave kernel's whole rounds) can take one more workgroup
+//     that builds the attention's work-unit table instead of taking tiles,
+//     on a CU that would otherwise idle; the tiles are dealt over the other
+//     workgroups.
 #include "attn_units.hpp"
 #include "gs_device.hpp"
 
