@@ -110,8 +110,11 @@ constexpr int UNIT_TABLE_LDS_INTS = UNIT_BINS + 16;
 // placement pass over the sequences, blockDim.x sequences at a time.  The
 // units of a sequence come in two runs of equal cost (those of its full
 // blocks, those of its last block), each counted and placed with one LDS
-// atomic.  lds: UNIT_TABLE_LDS_INTS ints.
-__device__ inline void build_unit_table(const UnitTableJob& j, int* lds) {
+// atomic.  lds: UNIT_TABLE_LDS_INTS ints.  Not inlined: inside a GEMM
+// kernel (the side job of its small-tile launch) the inlined builder
+// slowed the GEMM's own code.
+static __device__ __attribute__((noinline)) void build_unit_table(const UnitTableJob& j,
+                                                                  int* lds) {
   int* next = lds;                  // per cost bin: count, then next free position
   int* wsum = lds + UNIT_BINS;      // per wave: the count of its threads' bins
   const int T = blockDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

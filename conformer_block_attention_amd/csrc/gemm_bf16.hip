@@ -172,10 +172,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
 
   // With a job, the grid's last workgroup builds the attention's work-unit
   // table instead of taking tiles (a launch of fewer tiles than CUs runs it
-  // on a CU that would otherwise idle).
-  if (job.table && blockIdx.x == gridDim.x - 1) {
-    build_unit_table(job, (int*)smem);
-    return;
+  // on a CU that would otherwise idle).  Only the projection's launch
+  // carries one; the residual instantiations leave the code out (inlined
+  // there, it slowed out_proj's small-tile launch by about 15 %).
+  if constexpr (!RESID) {
+    if (job.table && blockIdx.x == gridDim.x - 1) {
+      build_unit_table(job, (int*)smem);
+      return;
+    }
   }
 
   const int tid = threadIdx.x;
