@@ -113,7 +113,7 @@ constexpr int UNIT_TABLE_LDS_INTS = UNIT_BINS + 16;
 // atomic.  lds: UNIT_TABLE_LDS_INTS ints.  Not inlined: inside a GEMM
 // kernel (the side job of its small-tile launch) the inlined builder
 // slowed the GEMM's own code.
-static __device__ __attribute__((noinline)) void build_unit_table(const UnitTableJob& j,
+static __device__ __attribute__((noinline)) void build_unit_table(UnitTableJob j,
                                                                   int* lds) {
   int* next = lds;                  // per cost bin: count, then next free position
   int* wsum = lds + UNIT_BINS;      // per wave: the count of its threads' bins
