@@ -75,8 +75,9 @@ typedef struct {
                               ignored, contents on return are unspecified */
   size_t workspace_bytes;
   /* Optional (may be NULL): four events the library records on `stream`
-     before the projection kernel, after it, after the attention kernel and
-     after the output-projection kernel, for per-kernel timing. */
+     before the projection, after it, after the attention and after the
+     output projection, for per-step timing (each event between two
+     kernels adds an idle gap of a few microseconds on the GPU). */
   hipEvent_t* kernel_events;
   /* 0, or GS_FWD_REUSE_UNIT_TABLE (gs_block_mhsa_fwd only, bf16): the
      workspace already holds the attention work-unit table that an earlier
@@ -104,8 +105,13 @@ size_t gs_block_mhsa_workspace_bytes(int64_t total_frames, int32_t d_model, gs_d
  *   out        [N][d]    result; may equal x (in place); any other overlap is invalid
  *   stream               HIP stream to enqueue on (0 = null stream)
  *   desc                 sizes, dtype, workspace (see gs_mhsa_desc)
- * Three kernels run in stream order: projection, block attention, output
- * projection with the residual.
+ * Three steps run in stream order, each one or two kernel launches: the
+ * projection, the block attention (with the build of its work-unit table
+ * from cu_seqlens, done in a spare workgroup of the projection's second
+ * launch when it has one, else by a kernel of its own), and the output
+ * projection with the residual.  Only kernels are enqueued (no memset, no
+ * host synchronisation unless GSATTN_DEBUG_CHECKS=1), so the call can be
+ * captured in a HIP graph.
  */
 gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void* Wqkv,
                             const void* Wo, int32_t block_frames, int32_t heads, void* out,
