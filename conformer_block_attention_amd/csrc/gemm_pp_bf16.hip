@@ -30,7 +30,9 @@
 //     through 8 KB of LDS (the 32 KB the ring leaves free, one area per wave
 //     of a group; the two groups use them in different phases), so that each
 //     store writes 8 whole 128-byte rows: stores of 32 rows x 32 bytes, the
-//     MFMA layout, cost the projection about 2.5 % more.  out_proj loads the
+//     MFMA layout, cost the projection about 2.5 % more.  These whole-row
+//     stores are non-temporal, so the output does not push the operand
+//     slices out of L2.  out_proj loads the
 //     residual in the piece layout and adds it in fp32 before the one RNE
 //     rounding.
 //   * tile order: all tiles are ordered in groups of 8 panels (256-row
@@ -55,6 +57,7 @@ namespace pp {
 
 constexpr int BM = 256;
 constexpr int BK = 64;           // K width of a ring stage
+constexpr int kCachePolicyNT = 2;  // buffer-store cache policy bit: non-temporal
 constexpr int NST = 2;           // ring stages
 constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
@@ -339,7 +342,11 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
               const int c8 = j * 4 + gp * 2 + half;
               xt[r * 8 + (c8 ^ (r & 7))] = u32x4_t{x0, x1, y0, y1};
             }
-        // one per-lane offset; the row step goes in the uniform soffset
+        // one per-lane offset; the row step goes in the uniform soffset.
+        // The stores are non-temporal (cache policy nt): a round of tiles
+        // writes as much output per XCD as its L2 holds, and with the
+        // default policy those lines pushed out the operand slices the next
+        // tiles read.
         const unsigned st_base =
             (unsigned)((wm * 128 + (lane >> 3)) * Nc + wn * WN + (lane & 7) * 8) * 2u;
 #pragma unroll
@@ -347,7 +354,8 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
           const int r = s * 8 + (lane >> 3);
           const int c8 = lane & 7;
           const u32x4_t v = xt[r * 8 + (c8 ^ (r & 7))];
-          __builtin_amdgcn_raw_buffer_store_b128(v, out_rs, st_base, (h * 64 + s * 8) * Nc * 2, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, out_rs, st_base, (h * 64 + s * 8) * Nc * 2,
+                                                 kCachePolicyNT);
         }
       }
     } else
