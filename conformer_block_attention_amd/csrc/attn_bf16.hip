@@ -788,15 +788,17 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           // Overflow: a non-finite row sum or accumulator (inf or NaN: all
           // exponent bits set) flags the item for the exact recomputation.
           {
+            // (whole vectors are reinterpreted: clang lowers a bit cast of
+            // one vector element as a read of element 0)
             unsigned big = 0;
 #pragma unroll
             for (int tt = 0; tt < QT; ++tt) {
-              big = max(big, __builtin_bit_cast(unsigned, lsum[tt][0]) & 0x7fffffffu);
+              big = max(big, __builtin_bit_cast(u32x4, lsum[tt]).x & 0x7fffffffu);
 #pragma unroll
-              for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  big = max(big, __builtin_bit_cast(unsigned, oacc[tt][dt][i]) & 0x7fffffffu);
+              for (int dt = 0; dt < 8; ++dt) {
+                const u32x4 u = __builtin_bit_cast(u32x4, oacc[tt][dt]) & 0x7fffffffu;
+                big = max(big, max(max(u.x, u.y), max(u.z, u.w)));
+              }
             }
             if (__builtin_amdgcn_ballot_w64(big >= 0x7f800000u) != 0 && lane == 0) {
               atomicOr(&ovf[uidx], 1ull << h);

@@ -187,6 +187,43 @@ def test_stage_block_attn_large_logits(orc):
     assert worst <= 1.0, worst
 
 
+def test_stage_block_attn_overflow_in_any_accumulator_column(orc):
+    """An item whose accumulators overflow in some output columns only, with
+    finite row sums, takes the exact fallback whatever columns they are.  A
+    lane of the bf16 kernel holds four consecutive head columns of a row in
+    one accumulator vector (column mod 4 = element), and the overflow check
+    must read all four.  Head h: queries 6, keys 0 but key 50 of each block
+    0.306 (weight 2^30 against the first chunk's reference), V = 1e30 in the
+    columns congruent to h mod 4 and N(0, 1) elsewhere."""
+    G.print_case("stage_block_attn_overflow_in_any_accumulator_column")
+    d, H, B = 512, 4, 200
+    lengths = [200, 130]
+    n = int(np.sum(lengths))
+    g = torch.Generator().manual_seed(23)
+    qkv = torch.randn(n, 3 * d, generator=g)
+    rel = np.concatenate([np.arange(ln) for ln in lengths]) % B
+    for h in range(H):
+        qkv[:, h * 128:(h + 1) * 128] = 6.0
+        kh = slice(d + h * 128, d + (h + 1) * 128)
+        qkv[:, kh] = 0.0
+        qkv[torch.from_numpy(rel == 50), kh] = 0.306
+        cols = 2 * d + h * 128 + np.arange(h, 128, 4)
+        qkv[:, torch.from_numpy(cols)] = 1e30
+    qkv_cpu = qkv.to(torch.bfloat16)
+    cu = workloads.cu_seqlens(lengths)
+    o = gsattn.block_attn(qkv_cpu.to(G.dev()), torch.from_numpy(cu).to(G.dev()), H, B)
+    torch.cuda.synchronize()
+    ref = orc.block_attn(qkv_cpu, cu, H, B)
+    got = o.double().cpu().numpy()
+    assert np.all(np.isfinite(ref))
+    assert np.all(np.isfinite(got)), [h for h in range(H)
+                                      if not np.all(np.isfinite(got[:, h * 128:(h + 1) * 128]))]
+    bound = _attn_bound(qkv_cpu.double().numpy(), cu, H, B, ref, torch.bfloat16)
+    worst = float(np.max(np.abs(got - ref) / bound))
+    print(f"  worst error / bound = {worst:.3f}", flush=True)
+    assert worst <= 1.0, worst
+
+
 def test_stage_block_attn_many_overflowed_items(orc):
     """More overflowed items per workgroup than its list of flagged items
     holds (64), so the exact recompute scans every item's flag word; and
