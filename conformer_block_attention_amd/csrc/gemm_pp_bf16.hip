@@ -26,15 +26,15 @@
 //     barrier makes them visible to all.
 //   * output: a cross-lane swap (v_permlane32_swap) joins lane l's and lane
 //     l+32's 4-column halves of the transposed accumulator tile into 16-byte
-//     row pieces.  Without a residual each wave then transposes its pieces
-//     through 8 KB of LDS (the 32 KB the ring leaves free, one area per wave
-//     of a group; the two groups use them in different phases), so that each
-//     store writes 8 whole 128-byte rows: stores of 32 rows x 32 bytes, the
-//     MFMA layout, cost the projection about 2.5 % more.  These whole-row
-//     stores are non-temporal, so the output does not push the operand
-//     slices out of L2.  out_proj loads the
-//     residual in the piece layout and adds it in fp32 before the one RNE
-//     rounding.
+//     row pieces.  Each wave then transposes its pieces through 8 KB of LDS
+//     (the 32 KB the ring leaves free, one area per wave of a group; the two
+//     groups use them in different phases), so that each store writes 8
+//     whole 128-byte rows: stores of 32 rows x 32 bytes, the MFMA layout,
+//     cost qkv_proj about 2.5 % and out_proj about 4 % more.  These
+//     whole-row stores are non-temporal, so the output does not push the
+//     operand slices out of L2.  out_proj transposes the fp32 sums (32 rows
+//     at a time), loads the residual in the same whole-row layout and adds
+//     it in fp32 before the one RNE rounding.
 //   * tile order: all tiles are ordered in groups of 8 panels (256-row
 //     strips), panel fastest within a group.  The 8 XCDs receive workgroup
 //     ids round-robin; each XCD owns one eighth of that order (a contiguous
@@ -166,9 +166,10 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
   constexpr int NOUT = TI * TJ * 2;                 // 16-byte output pieces per lane per tile
   static_assert(BN % 128 == 0 || BN == 384, "tile width");
   static_assert((KK == 1 || KK == 2) && WN % 32 == 0, "phase and tile shape");
-  // (without a residual: 8 KB per wave of a group after the ring, for the
-  // transpose of finished pieces into whole output rows)
-  constexpr int XT_ELEMS = RESID ? 0 : 4 * 4096;
+  static_assert(WN == 64, "the output transpose writes 128-byte wave rows");
+  // 8 KB per wave of a group after the ring, for the transpose of finished
+  // pieces into whole output rows
+  constexpr int XT_ELEMS = 4 * 4096;
   __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STAGE + XT_ELEMS];
 
   const int lane = threadIdx.x & 63;
@@ -299,30 +300,33 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
   auto store_tile = [&](int m0, int n0) __attribute__((always_inline)) {
     m0 = __builtin_amdgcn_readfirstlane(m0);
     n0 = __builtin_amdgcn_readfirstlane(n0);
-    unsigned ro[TI];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-      ro[i] = (unsigned)((wm * 128 + i * 32 + frag_row) * Nc + wn * WN + half * 8) * 2u;
     // bytes from the tile's origin to the end of its last row below M
     const unsigned tile_bytes = (unsigned)(min(M - m0, BM) * Nc - n0) * 2u;
     const auto out_rs = buffer_rsrc(C + (size_t)m0 * Nc + n0, tile_bytes);
-    // the residual pieces, all loaded first (the fragments are dead here)
-    u32x4_t rres[RESID ? TI * TJ * 2 : 1];
+    // Whole-row addressing: 16-byte piece lane % 8 of row 8s + lane / 8 of
+    // the wave's 128 rows; one per-lane offset, the row step in the uniform
+    // soffset.  Each access covers 8 whole 128-byte rows.
+    const unsigned st_base =
+        (unsigned)((wm * 128 + (lane >> 3)) * Nc + wn * WN + (lane & 7) * 8) * 2u;
+    // the residual rows, all loaded first (the fragments are dead here)
+    u32x4_t rres[RESID ? NOUT : 1];
     if constexpr (RESID) {
       const auto res_rs = buffer_rsrc(R + (size_t)m0 * Nc + n0, tile_bytes);
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int q = 0; q < TJ * 2; ++q)
-          rres[i * TJ * 2 + q] = __builtin_amdgcn_raw_buffer_load_b128(
-              res_rs, ro[i] + ((q >> 1) * 32 + (q & 1) * 16) * 2, 0, 0);
+      for (int k = 0; k < NOUT; ++k)
+        rres[k] = __builtin_amdgcn_raw_buffer_load_b128(res_rs, st_base, k * 8 * Nc * 2, 0);
     }
+    // The wave transposes its pieces through its own 8 KB LDS area: it reads
+    // only what it wrote itself (LDS keeps one wave's accesses in order), and
+    // the other group uses the area only after the next barrier.  The
+    // stores are non-temporal (cache policy nt): a round of tiles writes as
+    // much output per XCD as its L2 holds, and with the default policy those
+    // lines pushed out the operand slices the next tiles read.
+    GS_LDS u32x4_t* xt = (GS_LDS u32x4_t*)&smem[NST * STAGE] + (wave & 3) * 512;
     if constexpr (!RESID) {
-      // rows of 8 pieces, piece c of row r at c ^ (r mod 8): the 32 rows a
-      // write touches and the 8 pieces a read takes hit distinct banks.  The
-      // wave reads only what it wrote itself (LDS keeps one wave's accesses in
-      // order); the other group uses the area only after the next barrier.
-      GS_LDS u32x4_t* xt = (GS_LDS u32x4_t*)&smem[NST * STAGE] + (wave & 3) * 512;
+      // bf16, 64 rows at a time: rows of 8 pieces, piece c of row r at
+      // c ^ (r mod 8), so the 32 rows a write touches and the 8 pieces a
+      // read takes hit distinct banks.
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -342,13 +346,6 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
               const int c8 = j * 4 + gp * 2 + half;
               xt[r * 8 + (c8 ^ (r & 7))] = u32x4_t{x0, x1, y0, y1};
             }
-        // one per-lane offset; the row step goes in the uniform soffset.
-        // The stores are non-temporal (cache policy nt): a round of tiles
-        // writes as much output per XCD as its L2 holds, and with the
-        // default policy those lines pushed out the operand slices the next
-        // tiles read.
-        const unsigned st_base =
-            (unsigned)((wm * 128 + (lane >> 3)) * Nc + wn * WN + (lane & 7) * 8) * 2u;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const int r = s * 8 + (lane >> 3);
@@ -358,49 +355,59 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
                                                  kCachePolicyNT);
         }
       }
-    } else
+    } else {
+      // fp32, 32 rows at a time (the residual is added to the unrounded
+      // sums): rows of 16 four-column chunks, chunk c of row r at
+      // c ^ (r mod 16), so the 16 rows of a write and the 2 x 8 chunks of a
+      // read hit distinct banks.
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
+      for (int i = 0; i < TI; ++i) {
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          const f32x16& a = acc[i][j];
-          u32x4_t piece;
-          if constexpr (RESID) {
+          for (int gp = 0; gp < 2; ++gp) {
+            const f32x16& a = acc[i][j];
             unsigned x[4], y[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+              // (through float copies: clang lowers a bit cast of a vector
+              // element as a read of element 0)
               const float fx = a[gp * 8 + e], fy = a[gp * 8 + 4 + e];
               x[e] = __builtin_bit_cast(unsigned, fx);
               y[e] = __builtin_bit_cast(unsigned, fy);
               swap_lo_hi(x[e], y[e]);
             }
-            // columns 0..3 of the piece are x[0..3], columns 4..7 are y[0..3]
-            const u32x4_t r = rres[(i * TJ + j) * 2 + gp];
-            unsigned w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const unsigned rv = r[e];  // bf16 pair: columns 2e, 2e+1 of the piece
-              const float r0 = __builtin_bit_cast(float, rv << 16);
-              const float r1 = __builtin_bit_cast(float, rv & 0xFFFF0000u);
-              const float v0 = __builtin_bit_cast(float, e < 2 ? x[2 * e] : y[2 * e - 4]);
-              const float v1 = __builtin_bit_cast(float, e < 2 ? x[2 * e + 1] : y[2 * e - 3]);
-              w[e] = pack_bf16x2(v0 + r0, v1 + r1);
-            }
-            piece = u32x4_t{w[0], w[1], w[2], w[3]};
-          } else {
-            unsigned x0 = pack_bf16x2(a[gp * 8 + 0], a[gp * 8 + 1]);
-            unsigned x1 = pack_bf16x2(a[gp * 8 + 2], a[gp * 8 + 3]);
-            unsigned y0 = pack_bf16x2(a[gp * 8 + 4], a[gp * 8 + 5]);
-            unsigned y1 = pack_bf16x2(a[gp * 8 + 6], a[gp * 8 + 7]);
-            swap_lo_hi(x0, y0);
-            swap_lo_hi(x1, y1);
-            piece = u32x4_t{x0, x1, y0, y1};
+            // columns 0..3 of the piece are x[0..3] (chunk c), 4..7 are y[0..3]
+            const int r = frag_row;
+            const int c = (j * 4 + gp * 2 + half) * 2;
+            xt[r * 16 + (c ^ (r & 15))] = u32x4_t{x[0], x[1], x[2], x[3]};
+            xt[r * 16 + ((c + 1) ^ (r & 15))] = u32x4_t{y[0], y[1], y[2], y[3]};
           }
-          __builtin_amdgcn_raw_buffer_store_b128(piece, out_rs, ro[i] + (j * 32 + gp * 16) * 2,
-                                                 0, 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = s * 8 + (lane >> 3);
+          const int c = (lane & 7) * 2;
+          const u32x4_t lo = xt[r * 16 + (c ^ (r & 15))];
+          const u32x4_t hi = xt[r * 16 + ((c + 1) ^ (r & 15))];
+          const u32x4_t rv = rres[i * 4 + s];
+          // the 8 sums as plain words (columns 0..7 of the piece)
+          const unsigned v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          unsigned w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // bf16 pair of the residual: columns 2e, 2e+1 of the piece
+            const unsigned re = rv[e];
+            const float r0 = __builtin_bit_cast(float, re << 16);
+            const float r1 = __builtin_bit_cast(float, re & 0xFFFF0000u);
+            const float v0 = __builtin_bit_cast(float, v[2 * e]);
+            const float v1 = __builtin_bit_cast(float, v[2 * e + 1]);
+            w[e] = pack_bf16x2(v0 + r0, v1 + r1);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[0], w[1], w[2], w[3]}, out_rs,
+                                                 st_base, (i * 32 + s * 8) * Nc * 2,
+                                                 kCachePolicyNT);
         }
+      }
     }
     ops += NOUT + (RESID ? NOUT : 0);
   };
