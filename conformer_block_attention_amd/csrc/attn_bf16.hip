@@ -810,14 +810,21 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
           // +3 of its row.  For a pair of tiles dt, dt+1, v_permlane16_swap
           // trades the odd lane groups' dt values for the even groups' dt+1
           // values, so an even group g4 ends with dh dt*16 + 4*g4 .. +7 and an
-          // odd group with dh (dt+1)*16 + 4*(g4-1) .. +7.
+          // odd group with dh (dt+1)*16 + 4*(g4-1) .. +7: piece k = dt/2 of
+          // the lane's row, 16-byte chunk 4k + sg of the row's 16, with
+          // sg = (g4 & 1) * 2 + g4 / 2.
+          // Stores then write whole 128-byte row halves: lanes l16 and l16^8
+          // trade pieces (DPP row_ror:8), so that store (H, b) gives lane
+          // (g4, l16) chunk 8H + 4 (l16 / 8) + sg of row (l16 mod 8) + 8b,
+          // i.e. 8 rows x 128 bytes per instruction instead of 16 x 64.
           const int orow = row0 + q0 + rslot * ATT_QW;
+          const int hb = l16 >> 3;
+          const int sg = (g4 & 1) * 2 + (g4 >> 1);
 #pragma unroll
           for (int tt = 0; tt < QT; ++tt) {
             if (tt * 16 >= nval) continue;  // wave-uniform
             const float inv = 1.f / lsum[tt][0];
-            bf16* op = O + (size_t)(orow + tt * 16 + l16) * d + h * DH + (g4 & 1) * 16 + (g4 >> 1) * 8;
-            const bool row_ok = tt * 16 + l16 < nval;
+            u32x4 pc[4];
 #pragma unroll
             for (int dt = 0; dt < 8; dt += 2) {
               unsigned x0 = pack_bf16x2(oacc[tt][dt][0] * inv, oacc[tt][dt][1] * inv);
@@ -826,7 +833,24 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void block_attn_bf16_kernel(
               unsigned y1 = pack_bf16x2(oacc[tt][dt + 1][2] * inv, oacc[tt][dt + 1][3] * inv);
               swap_row_pairs(x0, y0);
               swap_row_pairs(x1, y1);
-              if (row_ok) *(u32x4*)(op + dt * 16) = u32x4{x0, x1, y0, y1};
+              pc[dt >> 1] = u32x4{x0, x1, y0, y1};
+            }
+#pragma unroll
+            for (int H = 0; H < 2; ++H) {
+              // the piece the partner l16^8 stores: 2H + 1 from the lower
+              // half, 2H from the upper
+              const u32x4 send = hb ? pc[2 * H] : pc[2 * H + 1];
+              u32x4 recv;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                recv[e] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)send[e], 0x128, 0xf, 0xf, false);
+#pragma unroll
+              for (int b = 0; b < 2; ++b) {
+                const u32x4 v = hb == b ? pc[2 * H + b] : recv;
+                const int rr = tt * 16 + (l16 & 7) + 8 * b;
+                if (rr < nval)
+                  *(u32x4*)(O + (size_t)(orow + rr) * d + h * DH + (8 * H + 4 * hb + sg) * 8) = v;
+              }
             }
           }
         }
