@@ -108,6 +108,37 @@ __global__ __launch_bounds__(1024) void lengths_prefix_kernel(const int* __restr
   if (tid == 0) cu[0] = 0;
 }
 
+// Row copies of the padded-bucket path: ZP_ROWS rows of one bucket per
+// workgroup, viewed as one run of nrows * pieces 16-byte pieces.  Each
+// thread issues ZP_PER loads before its stores, so a workgroup keeps
+// ZP_PER * 256 pieces (32 KB) in flight instead of one 2 KB row.
+constexpr int ZP_PER = 8;
+typedef unsigned int zp_u32x4 __attribute__((ext_vector_type(4)));
+template <class SrcRow, class DstRow>
+__device__ __forceinline__ void copy_row_run(int nrows, int pieces, SrcRow src_row,
+                                             DstRow dst_row) {
+  const int total = nrows * pieces;
+  for (int p0 = 0; p0 < total; p0 += ZP_PER * 256) {
+    zp_u32x4 v[ZP_PER];
+#pragma unroll
+    for (int k = 0; k < ZP_PER; ++k) {
+      const int p = p0 + k * 256 + (int)threadIdx.x;
+      const int r = p / pieces;
+      v[k] = zp_u32x4{0u, 0u, 0u, 0u};
+      if (p < total && dst_row(r)) v[k] = *(const zp_u32x4*)(src_row(r) + (p - r * pieces));
+    }
+#pragma unroll
+    for (int k = 0; k < ZP_PER; ++k) {
+      const int p = p0 + k * 256 + (int)threadIdx.x;
+      const int r = p / pieces;
+      if (p < total) {
+        uint4* d = dst_row(r);
+        if (d) *(zp_u32x4*)(d + (p - r * pieces)) = v[k];
+      }
+    }
+  }
+}
+
 // Valid rows of the buckets, packed: xp[cu[b] + t] = x[b*T + t], t < len[b].
 // Grid (ceil(T / ZP_ROWS), S); rows of `pieces` 16-byte pieces.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
@@ -118,12 +149,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   int l = len[b];
   l = l < 0 ? 0 : (l > T ? T : l);
   const int t0 = blockIdx.x * ZP_ROWS;
-  const int t1 = min(t0 + ZP_ROWS, l);
-  for (int t = t0; t < t1; ++t) {
-    const uint4* src = x + ((size_t)b * T + t) * pieces;
-    uint4* dst = xp + ((size_t)cu[b] + t) * pieces;
-    for (int i = threadIdx.x; i < pieces; i += blockDim.x) dst[i] = src[i];
-  }
+  const int n = min(ZP_ROWS, l - t0);
+  if (n <= 0) return;
+  const uint4* src = x + ((size_t)b * T + t0) * pieces;
+  uint4* dst = xp + ((size_t)cu[b] + t0) * pieces;
+  copy_row_run(
+      n, pieces, [=](int r) { return src + (size_t)r * pieces; },
+      [=](int r) { return dst + (size_t)r * pieces; });
 }
 
 // out[b*T + t] = outp[cu[b] + t] for t < len[b], x[b*T + t] for padding rows.
@@ -136,14 +168,16 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
   int l = len[b];
   l = l < 0 ? 0 : (l > T ? T : l);
   const int t0 = blockIdx.x * ZP_ROWS;
-  const int t1 = min(t0 + ZP_ROWS, T);
-  for (int t = t0; t < t1; ++t) {
-    const size_t row = (size_t)b * T + t;
-    const uint4* src = t < l ? outp + ((size_t)cu[b] + t) * pieces : x + row * pieces;
-    uint4* dst = out + row * pieces;
-    if (src == dst) continue;  // (in place, padding row)
-    for (int i = threadIdx.x; i < pieces; i += blockDim.x) dst[i] = src[i];
-  }
+  const int n = min(ZP_ROWS, T - t0);
+  if (n <= 0) return;
+  const size_t row0 = (size_t)b * T + t0;
+  const uint4* valid = outp + ((size_t)cu[b] + t0) * pieces;
+  const bool in_place = x == out;
+  copy_row_run(
+      n, pieces,
+      [=](int r) { return t0 + r < l ? valid + (size_t)r * pieces : x + (row0 + r) * pieces; },
+      // (in place, a padding row already holds x)
+      [=](int r) { return t0 + r < l || !in_place ? out + (row0 + r) * pieces : nullptr; });
 }
 }  // namespace gs
 

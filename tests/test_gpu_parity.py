@@ -493,6 +493,42 @@ def test_padded_garbage_in_padding_does_not_leak():
     assert torch.equal(out2.reshape(-1, d)[~vt], x2[~vt])
 
 
+@pytest.mark.parametrize("S,T,full,last", [(20, 1000, 970, 954), (24, 1000, 975, 959)])
+def test_padded_matches_packed_at_small_tile_sizes(orc, S, T, full, last):
+    """Padded buckets whose valid rows, packed, make the packed entry point
+    split its projections between the two-wave kernel and a round of small
+    tiles of each remaining row tile (19 384 rows: out_proj's rest as
+    128-row tiles; 23 384: qkv_proj's as 192-row and out_proj's as 256-row
+    tiles; the 128 x 800 workload covers 64 and 192).  The padded path runs
+    each projection as one launch with the row count read on the device, so
+    its valid rows equal the packed ones bit for bit only if every row tile
+    of the small-tile kernel sums exactly as the two-wave kernel does.
+    Padding rows equal x, and two buckets match the oracle."""
+    d, H, B = 1024, 8, 200
+    lengths = np.array([full] * (S - 1) + [last], dtype=np.int64)
+    G.print_case("padded_matches_packed", S=S, T=T, valid=int(lengths.sum()))
+    g = torch.Generator().manual_seed(31)
+    x = (torch.randn(S * T, d, generator=g) * 0.5).to(torch.bfloat16)
+    case = workloads.custom_case(lengths, d, H, B, torch.bfloat16, seed=31)
+    wqkv, wo = (w.to(G.dev()) for w in case.weights[0])
+    xd = x.to(G.dev())
+    lens = torch.from_numpy(lengths.astype(np.int32)).to(G.dev())
+    out = gsattn.block_mhsa_fwd_padded(xd.view(S, T, d), lens, wqkv, wo, B, H).reshape(-1, d)
+    torch.cuda.synchronize()
+    valid = torch.from_numpy((np.arange(S * T) % T) < np.repeat(lengths, T)).to(G.dev())
+    assert torch.equal(out[~valid], xd[~valid]), "padding rows differ from x"
+    cu = torch.from_numpy(workloads.cu_seqlens(lengths)).to(G.dev())
+    packed = G.run(xd[valid].contiguous(), cu, wqkv, wo, B, H)
+    assert torch.equal(packed, out[valid]), "valid rows differ from the packed entry point"
+    for b in (0, S - 1):
+        rows = slice(b * T, b * T + int(lengths[b]))
+        ref = orc.block_mhsa(x[rows], workloads.cu_seqlens(lengths[b:b + 1]), case.weights[0][0],
+                             case.weights[0][1], B, H)
+        err = G.rel_err(out[rows].double().cpu().numpy(), ref)
+        print(f"  bucket {b}: err={err:.3e}", flush=True)
+        assert err <= G.BF16_TOL, (b, err)
+
+
 def test_padded_lengths_outside_the_bucket_are_clamped():
     """Lengths below 0 or above the bucket act as 0 and T (the documented
     clamp), bit for bit."""
