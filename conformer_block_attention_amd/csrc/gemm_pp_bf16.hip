@@ -71,6 +71,24 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // physical chunk c ^ ((r / 2) mod 8): those rows then hit 16 distinct slots.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
+// Row tables are read through the constant address space, so that a
+// wave-uniform address becomes a scalar load (counted in lgkmcnt, apart from
+// the vector-memory count that paces the copies).
+#define GS_CONST __attribute__((address_space(4)))
+typedef int int8v __attribute__((ext_vector_type(8)));
+// e[i] for a per-lane i in 0..7 (a select chain: no dynamic vector index)
+__device__ __forceinline__ int pick8(int8v e, int i) {
+  int v = e[0];
+  v = i == 1 ? e[1] : v;
+  v = i == 2 ? e[2] : v;
+  v = i == 3 ? e[3] : v;
+  v = i == 4 ? e[4] : v;
+  v = i == 5 ? e[5] : v;
+  v = i == 6 ? e[6] : v;
+  v = i == 7 ? e[7] : v;
+  return v;
+}
+
 // Global->LDS copies of one [ROWS x BK] operand tile per stage by 8 waves:
 // copy j of wave w fills LDS rows (j*8 + w)*8 ... +7 (1 KB); lane i writes
 // row + i/8 at physical chunk i%8.  Per-lane byte offsets from the tile's
@@ -90,6 +108,22 @@ struct Copy {
       int gr = row0 + r;
       if (CLAMP) gr = gr < row_limit ? gr : row_limit - 1;
       off[j] = (unsigned)((gr - row0) * ld + c * 8) * 2u;
+    }
+  }
+  // Rows through a table (row r of the product is row rows[r] of the
+  // operand; rows at or past row_limit read row last_src): offsets from the
+  // operand's first row.  The entries of one copy's 8 rows come by one
+  // scalar load.
+  __device__ __forceinline__ void init_rows(int row0, int row_limit, int ld, int wave, int lane,
+                                            const GS_CONST int* rows, int last_src) {
+#pragma unroll
+    for (int j = 0; j < NOFF; ++j) {
+      const int rb = row0 + (j * 8 + wave) * 8;  // uniform
+      const int r = (j * 8 + wave) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      int src = pick8(*(const GS_CONST int8v*)(rows + rb), lane >> 3);
+      if (rb + (lane >> 3) >= row_limit) src = last_src;
+      off[j] = (unsigned)(src * ld + c * 8) * 2u;
     }
   }
   // copy j of this wave; tile: the tile's first row at this K step (uniform)
@@ -148,12 +182,21 @@ __device__ __forceinline__ void swap_lo_hi(unsigned& x, unsigned& y) {
 // group).  m_dev: if not null, the row count is read from device memory
 // instead of M (M then only bounds the grid), for row counts that exist only
 // on the device.
-template <int BN, bool RESID, int KK>
+template <int BN, bool RESID, int KK, bool ROWS = false>
 __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* R, bf16* C, int M,
-    int Nc, int K, const int* __restrict__ m_dev) {
+    int Nc, int K, const int* __restrict__ m_dev, const int* __restrict__ rows_table) {
   using namespace pp;
+  const int m_cap = M;  // rows the buffers hold (the row count's bound)
   if (m_dev) M = __builtin_amdgcn_readfirstlane(*m_dev);
+  // ROWS: a row table maps row r of the product to row rows[r] of A (without
+  // a residual) or of R and C (with one); rows at or past M read row
+  // rows[M - 1] of A, and their residual reads and stores are dropped.
+  const GS_CONST int* rows = (const GS_CONST int*)rows_table;
+  int last_src = 0;
+  if constexpr (ROWS) {
+    if (M > 0) last_src = rows[M - 1];
+  }
   using CopyA = Copy<BM, true>;   // activation rows: the last panel is ragged
   using CopyB = Copy<BN, false>;  // weight rows: Nc % BN == 0
   constexpr int WN = BN / 4;      // wave tile columns
@@ -225,9 +268,15 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
   const bf16* tA = nullptr;
   const bf16* tB = nullptr;
   auto set_issue_tile = [&]() __attribute__((always_inline)) {
-    tA = A + (size_t)is_panel * BM * K;
-    tB = W + (size_t)is_col * BN * K;
-    cpA.init(is_panel * BM, M, K, wave, lane);
+    if constexpr (ROWS && !RESID) {
+      tA = A;
+      tB = W + (size_t)is_col * BN * K;
+      cpA.init_rows(is_panel * BM, M, K, wave, lane, rows, last_src);
+    } else {
+      tA = A + (size_t)is_panel * BM * K;
+      tB = W + (size_t)is_col * BN * K;
+      cpA.init(is_panel * BM, M, K, wave, lane);
+    }
     cpB.init(is_col * BN, Nc, K, wave, lane);
   };
   set_issue_tile();
@@ -302,19 +351,47 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
     n0 = __builtin_amdgcn_readfirstlane(n0);
     // bytes from the tile's origin to the end of its last row below M
     const unsigned tile_bytes = (unsigned)(min(M - m0, BM) * Nc - n0) * 2u;
-    const auto out_rs = buffer_rsrc(C + (size_t)m0 * Nc + n0, tile_bytes);
-    // Whole-row addressing: 16-byte piece lane % 8 of row 8s + lane / 8 of
+    // Whole-row addressing: 16-byte piece lane % 8 of row 8k + lane / 8 of
     // the wave's 128 rows; one per-lane offset, the row step in the uniform
     // soffset.  Each access covers 8 whole 128-byte rows.
     const unsigned st_base =
         (unsigned)((wm * 128 + (lane >> 3)) * Nc + wn * WN + (lane & 7) * 8) * 2u;
+    // With a row table (residual and output rows elsewhere): one offset per
+    // row from the start of R and C, past the buffers' end for rows >= M.
+    constexpr bool SCATTER = ROWS && RESID;
+    unsigned roff[SCATTER ? NOUT : 1];
+    if constexpr (SCATTER) {
+#pragma unroll
+      for (int k = 0; k < NOUT; ++k) {
+        const int rb = m0 + wm * 128 + 8 * k;  // uniform
+        const int src = pick8(*(const GS_CONST int8v*)(rows + rb), lane >> 3);
+        roff[k] = rb + (lane >> 3) < M
+                      ? (unsigned)(src * Nc + n0 + wn * WN + (lane & 7) * 8) * 2u
+                      : 0xFFFFFFF0u;
+      }
+    }
+    // the output (and residual) through buffers over the tile's rows below
+    // M, or over all M_cap rows of C (and R) with a row table
+    auto rows_rsrc = [&](const bf16* base) __attribute__((always_inline)) {
+      if constexpr (SCATTER)
+        return buffer_rsrc(base, (unsigned)((size_t)m_cap * Nc * 2));
+      else
+        return buffer_rsrc(base + (size_t)m0 * Nc + n0, tile_bytes);
+    };
+    const auto out_rs = rows_rsrc(C);
     // the residual rows, all loaded first (the fragments are dead here)
     u32x4_t rres[RESID ? NOUT : 1];
     if constexpr (RESID) {
-      const auto res_rs = buffer_rsrc(R + (size_t)m0 * Nc + n0, tile_bytes);
+      const auto res_rs = rows_rsrc(R);
+      if constexpr (SCATTER) {
 #pragma unroll
-      for (int k = 0; k < NOUT; ++k)
-        rres[k] = __builtin_amdgcn_raw_buffer_load_b128(res_rs, st_base, k * 8 * Nc * 2, 0);
+        for (int k = 0; k < NOUT; ++k)
+          rres[k] = __builtin_amdgcn_raw_buffer_load_b128(res_rs, roff[k], 0, 0);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NOUT; ++k)
+          rres[k] = __builtin_amdgcn_raw_buffer_load_b128(res_rs, st_base, k * 8 * Nc * 2, 0);
+      }
     }
     // The wave transposes its pieces through its own 8 KB LDS area: it reads
     // only what it wrote itself (LDS keeps one wave's accesses in order), and
@@ -403,9 +480,13 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
             const float v1 = __builtin_bit_cast(float, v[2 * e + 1]);
             w[e] = pack_bf16x2(v0 + r0, v1 + r1);
           }
-          __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[0], w[1], w[2], w[3]}, out_rs,
-                                                 st_base, (i * 32 + s * 8) * Nc * 2,
-                                                 kCachePolicyNT);
+          const u32x4_t piece = u32x4_t{w[0], w[1], w[2], w[3]};
+          if constexpr (SCATTER)
+            __builtin_amdgcn_raw_buffer_store_b128(piece, out_rs, roff[i * 4 + s], 0,
+                                                   kCachePolicyNT);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(piece, out_rs, st_base,
+                                                   (i * 32 + s * 8) * Nc * 2, kCachePolicyNT);
         }
       }
     }
@@ -527,7 +608,7 @@ static hipError_t pp_launch(const bf16* A, const bf16* W, const bf16* R, bf16* C
     const int mt = (rows + pp::BM - 1) / pp::BM;
     hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, RESID, 2>),
                        dim3(pp_persistent_grid(mt * (Nc / 256))), dim3(pp::THREADS), 0, stream, A,
-                       W, R, C, rows, Nc, K, md);
+                       W, R, C, rows, Nc, K, md, nullptr);
   };
   if (m_dev) {
     launch(M, m_dev);
@@ -543,6 +624,29 @@ static hipError_t pp_launch(const bf16* A, const bf16* W, const bf16* R, bf16* C
                             tail_bm, stream, job);
   if (e == hipSuccess && job && job_done) *job_done = true;
   return e;
+}
+
+// Through a row table (row r of the product is row rows[r] of the operand
+// named below), with the row count m_dev on the device, at most M: one
+// launch.  Without R: C[r] = A[rows[r]] . W^T.  With R: C[rows[r]] =
+// R[rows[r]] + A[r] . W^T (M rows of R and C then lie anywhere among M_cap).
+// rows needs ceil(M / 256) * 256 readable entries, 32-byte aligned; byte
+// offsets into A (without R) or into R and C (with R) must fit 32 bits:
+// M_cap * Nc * 2 (with R) or M_cap * K * 2 (without) below 2^32 - 16.
+hipError_t launch_gemm_nt_bf16_pp_rows(const void* A, const void* W, const void* R, void* C,
+                                       int M, int M_cap, int Nc, int K, const int* m_dev,
+                                       const int* rows, hipStream_t stream) {
+  const int mt = (M + pp::BM - 1) / pp::BM;
+  const dim3 grid(pp_persistent_grid(mt * (Nc / 256)));
+  if (R)
+    hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, true, 2, true>), grid, dim3(pp::THREADS), 0,
+                       stream, (const bf16*)A, (const bf16*)W, (const bf16*)R, (bf16*)C, M_cap,
+                       Nc, K, m_dev, rows);
+  else
+    hipLaunchKernelGGL((gemm_pp_bf16_kernel<256, false, 2, true>), grid, dim3(pp::THREADS), 0,
+                       stream, (const bf16*)A, (const bf16*)W, (const bf16*)nullptr, (bf16*)C,
+                       M_cap, Nc, K, m_dev, rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_qkv_proj_bf16_pp(const void* x, const void* wqkv, void* qkv, int M, int d,

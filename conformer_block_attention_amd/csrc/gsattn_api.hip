@@ -33,6 +33,9 @@ hipError_t launch_bpe_pool_ctc(const void* logits, long long ld, const float* bl
                                hipStream_t stream);
 hipError_t launch_gemm_nt_bf16_pp(const void* A, const void* W, const void* R, void* C, int M,
                                   int Nc, int K, hipStream_t stream, const int* m_dev = nullptr);
+hipError_t launch_gemm_nt_bf16_pp_rows(const void* A, const void* W, const void* R, void* C,
+                                       int M, int M_cap, int Nc, int K, const int* m_dev,
+                                       const int* rows, hipStream_t stream);
 hipError_t launch_window_attn_bf16(const void* kv, const void* q, const int* cu, int S, int W,
                                    int nq, int heads, int dq, int window, void* table,
                                    void* o, hipStream_t stream);
@@ -178,6 +181,36 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
       [=](int r) { return t0 + r < l ? valid + (size_t)r * pieces : x + (row0 + r) * pieces; },
       // (in place, a padding row already holds x)
       [=](int r) { return t0 + r < l || !in_place ? out + (row0 + r) * pieces : nullptr; });
+}
+
+// The row table of the padded path: rows[cu[b] + t] = b*T + t for the valid
+// rows t < len[b] of bucket b (packed row -> padded row).  Grid
+// (ceil(T / 256), S).
+__global__ __launch_bounds__(256) void padded_rows_table_kernel(const int* __restrict__ len,
+                                                                const int* __restrict__ cu,
+                                                                int T, int* __restrict__ rows) {
+  const int b = blockIdx.y;
+  int l = len[b];
+  l = l < 0 ? 0 : (l > T ? T : l);
+  const int t = blockIdx.x * 256 + (int)threadIdx.x;
+  if (t < l) rows[cu[b] + t] = b * T + t;
+}
+
+// out[b*T + t] = x[b*T + t] for the padding rows t >= len[b] (out != x).
+__global__ __launch_bounds__(256) void copy_padding_rows_kernel(const uint4* __restrict__ x,
+                                                                const int* __restrict__ len,
+                                                                int T, int pieces,
+                                                                uint4* __restrict__ out) {
+  const int b = blockIdx.y;
+  int l = len[b];
+  l = l < 0 ? 0 : (l > T ? T : l);
+  const int t0 = max((int)blockIdx.x * ZP_ROWS, l);
+  const int n = min((int)blockIdx.x * ZP_ROWS + ZP_ROWS, T) - t0;
+  if (n <= 0) return;
+  const size_t row0 = (size_t)b * T + t0;
+  copy_row_run(
+      n, pieces, [=](int r) { return x + (row0 + r) * pieces; },
+      [=](int r) { return out + (row0 + r) * pieces; });
 }
 }  // namespace gs
 
@@ -524,15 +557,25 @@ gs_status gs_block_mhsa_fwd_noalloc(const void* x, const int32_t* cu_seqlens, co
   return gs_block_mhsa_fwd(x, cu_seqlens, Wqkv, Wo, block_frames, heads, out, stream, &desc);
 }
 
+// The bf16 padded path moves valid rows through a row table when byte
+// offsets into x and out fit the projection kernels' 32-bit offsets; larger
+// inputs pack the valid rows into the workspace instead.
+static bool padded_rows_by_table(int64_t rows, int32_t d_model) {
+  return (uint64_t)rows * (uint64_t)d_model * 2 < 0xFFFFFFF0ull;
+}
+
 size_t gs_block_mhsa_padded_workspace_bytes(int32_t num_seqs, int32_t bucket_frames,
                                             int32_t d_model, gs_dtype dtype) {
   if (num_seqs < 1 || bucket_frames < 1) return 0;
   const int64_t rows = (int64_t)num_seqs * bucket_frames;
   const size_t base = gs_block_mhsa_workspace_bytes(rows, d_model, dtype);
   if (base == 0) return 0;
-  // the valid rows packed (input and output) and their offsets
+  // the buckets' offsets, and either the row table (a 256-row panel of slack)
+  // or the valid rows packed (input and output)
+  const size_t offsets = align_up(4 * ((size_t)num_seqs + 1));
+  if (padded_rows_by_table(rows, d_model)) return base + offsets + align_up(4 * ((size_t)rows + 256));
   const size_t packed = align_up((size_t)rows * d_model * elem_size(dtype));
-  return base + 2 * packed + align_up(4 * ((size_t)num_seqs + 1));
+  return base + 2 * packed + offsets;
 }
 
 gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_t bucket_frames,
@@ -559,9 +602,47 @@ gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_
   const dim3 rows_grid((bucket_frames + gs::ZP_ROWS - 1) / gs::ZP_ROWS, desc->num_seqs);
   const int pieces = (int)((size_t)p.d * e / 16);
 
+  if (desc->dtype == GS_BF16 && p.d % 256 == 0 && padded_rows_by_table(p.N, p.d)) {
+    // Compact through a row table: the projection reads the valid rows of x
+    // straight from their buckets, the attention runs on the packed Q|K|V,
+    // out_proj reads the residual from x and writes each valid row to its
+    // bucket, and the padding rows are copied from x (none in place).  The
+    // row count exists only on the device.
+    char* ws = (char*)desc->workspace + gs_block_mhsa_workspace_bytes(p.N, p.d, desc->dtype);
+    const int S = desc->num_seqs;
+    int* cu = (int*)ws;
+    int* rows = (int*)(ws + align_up(4 * ((size_t)S + 1)));
+    GS_TRY(record(desc, 0, stream));
+    hipLaunchKernelGGL(gs::lengths_prefix_kernel, dim3(1), dim3(1024), 0, stream,
+                       (const int*)lengths, S, (int)bucket_frames, cu);
+    hipLaunchKernelGGL(gs::padded_rows_table_kernel, dim3((bucket_frames + 255) / 256, S),
+                       dim3(256), 0, stream, (const int*)lengths, (const int*)cu,
+                       (int)bucket_frames, rows);
+    GS_TRY(hip_status(hipGetLastError(), "row table launch"));
+    GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp_rows(x, Wqkv, nullptr, p.qkv, (int)p.N, (int)p.N,
+                                                      3 * p.d, p.d, cu + S, rows, stream),
+                      "qkv_proj launch"));
+    GS_TRY(record(desc, 1, stream));
+    GS_TRY(attn_spans(p.qkv, gs::SeqSpans{cu, 0}, S, p.N, p.d, heads, block_frames, desc->dtype,
+                      p.o, p.table, stream));
+    GS_TRY(record(desc, 2, stream));
+    GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp_rows(p.o, Wo, x, out, (int)p.N, (int)p.N, p.d,
+                                                      p.d, cu + S, rows, stream),
+                      "out_proj launch"));
+    if (out != x) {
+      hipLaunchKernelGGL(gs::copy_padding_rows_kernel, rows_grid, dim3(256), 0, stream,
+                         (const uint4*)x, (const int*)lengths, (int)bucket_frames, pieces,
+                         (uint4*)out);
+      GS_TRY(hip_status(hipGetLastError(), "padding rows launch"));
+    }
+    GS_TRY(record(desc, 3, stream));
+    return GS_OK;
+  }
+
   if (desc->dtype == GS_BF16 && p.d % 256 == 0) {
-    // Compact: pack the valid rows, run the packed sub-layer on them with
-    // the row count taken on the device, and unpack (padding rows copy x).
+    // Inputs too large for the row table's 32-bit offsets: pack the valid
+    // rows, run the packed sub-layer on them with the row count taken on the
+    // device, and unpack (padding rows copy x).
     char* ws = (char*)desc->workspace + gs_block_mhsa_workspace_bytes(p.N, p.d, desc->dtype);
     const size_t packed = align_up((size_t)p.N * p.d * e);
     void* xp = ws;

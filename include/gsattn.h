@@ -160,11 +160,17 @@ gs_status gs_block_mhsa_fwd_noalloc(const void* x, const int32_t* cu_seqlens, co
  * so the valid rows of `out` equal those of gs_block_mhsa_fwd on the same
  * sequences packed.  Padding rows are neither queries nor keys: their
  * attention output is zero, so out = x there (up to the sign of zero).  For
- * bf16 with d a multiple of 256 the valid rows are packed on the device,
- * run through the packed sub-layer (the projections take the row count from
- * device memory) and unpacked; otherwise the projections run over all S*T
- * rows and O's padding rows are zeroed.  The workspace is
- * gs_block_mhsa_padded_workspace_bytes(S, T, d, dtype) bytes.
+ * bf16 with d a multiple of 256 the valid rows run packed, with their count
+ * and a packed-to-padded row table built on the device: the Q|K|V
+ * projection reads them from their buckets, the attention runs on the
+ * packed Q|K|V, and out_proj reads the residual from x and writes each
+ * valid row into its bucket; padding rows are then copied from x (nothing
+ * to copy when out == x).  When S*T*d*2 bytes reach 4 GiB (beyond the
+ * projections' 32-bit offsets) the valid rows are packed into the
+ * workspace and unpacked instead.  Other dtypes and widths run the
+ * projections over all S*T rows and zero O's padding rows.  out may equal
+ * x.  The workspace is gs_block_mhsa_padded_workspace_bytes(S, T, d, dtype)
+ * bytes.
  */
 size_t gs_block_mhsa_padded_workspace_bytes(int32_t num_seqs, int32_t bucket_frames,
                                             int32_t d_model, gs_dtype dtype);

@@ -529,6 +529,59 @@ def test_padded_matches_packed_at_small_tile_sizes(orc, S, T, full, last):
         assert err <= G.BF16_TOL, (b, err)
 
 
+def test_padded_in_place():
+    """out == x on the padded path: out_proj reads each valid row's residual
+    from x and writes the row back in place, and padding rows stay as they
+    are; the result equals the out-of-place one bit for bit."""
+    d, H, B, T = 1024, 8, 200, 512
+    lengths = np.array([512, 0, 300, 77, 1, 511, 256, 200], dtype=np.int64)
+    S = len(lengths)
+    G.print_case("padded_in_place", S=S, T=T)
+    case = workloads.custom_case(lengths, d, H, B, torch.bfloat16, seed=41)
+    wqkv, wo = (w.to(G.dev()) for w in case.weights[0])
+    g = torch.Generator(device=G.dev()).manual_seed(41)
+    x = torch.randn(S, T, d, generator=g, device=G.dev()).to(torch.bfloat16)
+    lens = torch.from_numpy(lengths.astype(np.int32)).to(G.dev())
+    ref = gsattn.block_mhsa_fwd_padded(x, lens, wqkv, wo, B, H).clone()
+    y = x.clone()
+    gsattn.block_mhsa_fwd_padded(y, lens, wqkv, wo, B, H, out=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+
+
+def test_padded_pack_path_beyond_32bit_offsets(orc):
+    """S*T*d*2 above 4 GiB (2 100 buckets of 1 000 rows at d = 1 024): the
+    padded path packs the valid rows into the workspace instead of using the
+    row table.  Padding rows equal x, valid rows equal the packed entry point
+    bit for bit, and two buckets match the oracle."""
+    d, H, B, S, T = 1024, 8, 200, 2100, 1000
+    assert S * T * d * 2 >= 2 ** 32
+    rng = np.random.default_rng(43)
+    lengths = rng.integers(0, 40, size=S)
+    lengths[::300] = T
+    lengths[7] = 0
+    G.print_case("padded_pack_path", S=S, T=T, valid=int(lengths.sum()))
+    case = workloads.custom_case(lengths[:2], d, H, B, torch.bfloat16, seed=43)
+    wqkv, wo = (w.to(G.dev()) for w in case.weights[0])
+    g = torch.Generator(device=G.dev()).manual_seed(43)
+    x = (torch.randn(S * T, d, generator=g, device=G.dev()) * 0.5).to(torch.bfloat16)
+    lens = torch.from_numpy(lengths.astype(np.int32)).to(G.dev())
+    out = gsattn.block_mhsa_fwd_padded(x.view(S, T, d), lens, wqkv, wo, B, H).view(-1, d)
+    torch.cuda.synchronize()
+    valid = torch.from_numpy((np.arange(S * T) % T) < np.repeat(lengths, T)).to(G.dev())
+    assert torch.equal(out[~valid], x[~valid]), "padding rows differ from x"
+    cu = torch.from_numpy(workloads.cu_seqlens(lengths)).to(G.dev())
+    packed = G.run(x[valid].contiguous(), cu, wqkv, wo, B, H)
+    assert torch.equal(packed, out[valid]), "valid rows differ from the packed entry point"
+    for b in (0, 300):
+        rows = slice(b * T, b * T + int(lengths[b]))
+        ref = orc.block_mhsa(x[rows].cpu(), workloads.cu_seqlens(lengths[b:b + 1]),
+                             case.weights[0][0], case.weights[0][1], B, H)
+        err = G.rel_err(out[rows].double().cpu().numpy(), ref)
+        print(f"  bucket {b} ({int(lengths[b])} rows): err={err:.3e}", flush=True)
+        assert err <= G.BF16_TOL, (b, err)
+
+
 def test_padded_lengths_outside_the_bucket_are_clamped():
     """Lengths below 0 or above the bucket act as 0 and T (the documented
     clamp), bit for bit."""
