@@ -22,8 +22,9 @@
 //     8i + 2048k .. +7 (16-byte loads of bf16 logits) for each of its
 //     positions, keeps a running (max, index) per position, and the
 //     workgroup reduces them at the end.  With window 4 and stride 2 and
-//     positions of one sequence, each frame is loaded once and serves the
-//     two windows that hold it;
+//     positions of one sequence, each frame is loaded once by the workgroup
+//     and serves the two windows that hold it; the two frames neighbouring
+//     groups share come from L2 for the second (groups in order on one XCD);
 //   * decode: one wave per sequence, 64 positions at a time, ballot and
 //     prefix count to compact the kept tokens.
 #include "gs_device.hpp"
@@ -105,7 +106,14 @@ __global__ __launch_bounds__(PA_THREADS) void pooled_argmax_kernel(
   __shared__ float sv[PA_POS][PA_THREADS / 64];
   __shared__ int si[PA_POS][PA_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int p0 = blockIdx.x * PA_POS;
+  // Neighbouring groups of positions share frames (window 4, stride 2: the
+  // last two frames of one group are the first two of the next).  Workgroup
+  // ids reach the 8 XCDs round-robin, so consecutive groups are dealt to
+  // the workgroups of one XCD (wg, wg + 8, ...), which run at about the same
+  // time and find the shared frames in that XCD's L2.
+  const int G = (int)gridDim.x, wg = (int)blockIdx.x, G8 = G & ~7;
+  const int group = wg < G8 ? (wg & 7) * (G8 >> 3) + (wg >> 3) : wg;
+  const int p0 = group * PA_POS;
   int t0[PA_POS], nt[PA_POS];
   float w[PA_POS][PA_MAXWIN];
 #pragma unroll
