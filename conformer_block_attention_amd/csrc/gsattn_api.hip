@@ -185,10 +185,17 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
 
 // The row table of the padded path: rows[cu[b] + t] = b*T + t for the valid
 // rows t < len[b] of bucket b (packed row -> padded row).  Grid
-// (ceil(T / 256), S).
+// (ceil(T / 256), S + 1): the first workgroup of the last row of the grid
+// builds the attention's work-unit table (job) meanwhile.
 __global__ __launch_bounds__(256) void padded_rows_table_kernel(const int* __restrict__ len,
                                                                 const int* __restrict__ cu,
-                                                                int T, int* __restrict__ rows) {
+                                                                int T, int* __restrict__ rows,
+                                                                UnitTableJob job) {
+  if (blockIdx.y == gridDim.y - 1) {
+    __shared__ int lds[UNIT_TABLE_LDS_INTS];
+    if (blockIdx.x == 0) build_unit_table(job, lds);
+    return;
+  }
   const int b = blockIdx.y;
   int l = len[b];
   l = l < 0 ? 0 : (l > T ? T : l);
@@ -615,16 +622,19 @@ gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_
     GS_TRY(record(desc, 0, stream));
     hipLaunchKernelGGL(gs::lengths_prefix_kernel, dim3(1), dim3(1024), 0, stream,
                        (const int*)lengths, S, (int)bucket_frames, cu);
-    hipLaunchKernelGGL(gs::padded_rows_table_kernel, dim3((bucket_frames + 255) / 256, S),
+    // (the attention's unit table is built in the same launch)
+    const gs::UnitTableJob job = gs::attn_bf16_table_job(gs::SeqSpans{cu, 0}, S, p.N,
+                                                         block_frames, p.table);
+    hipLaunchKernelGGL(gs::padded_rows_table_kernel, dim3((bucket_frames + 255) / 256, S + 1),
                        dim3(256), 0, stream, (const int*)lengths, (const int*)cu,
-                       (int)bucket_frames, rows);
+                       (int)bucket_frames, rows, job);
     GS_TRY(hip_status(hipGetLastError(), "row table launch"));
     GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp_rows(x, Wqkv, nullptr, p.qkv, (int)p.N, (int)p.N,
                                                       3 * p.d, p.d, cu + S, rows, stream),
                       "qkv_proj launch"));
     GS_TRY(record(desc, 1, stream));
     GS_TRY(attn_spans(p.qkv, gs::SeqSpans{cu, 0}, S, p.N, p.d, heads, block_frames, desc->dtype,
-                      p.o, p.table, stream));
+                      p.o, p.table, stream, false));
     GS_TRY(record(desc, 2, stream));
     GS_TRY(hip_status(gs::launch_gemm_nt_bf16_pp_rows(p.o, Wo, x, out, (int)p.N, (int)p.N, p.d,
                                                       p.d, cu + S, rows, stream),
