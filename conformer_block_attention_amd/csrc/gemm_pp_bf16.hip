@@ -346,6 +346,26 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
   // the swap leaves lane l (< 32) with all 8 columns of group 2gp and lane
   // l+32 with all 8 of group 2gp+1: piece (i, j, gp) of a lane is row
   // wm*128 + i*32 + lane%32, columns wn*WN + j*32 + gp*16 + (lane/32)*8 .. +7.
+  // With a row table and a residual: one byte offset per access k (row
+  // 8k + lane / 8 of this wave's 128 rows of the finished tile) from the
+  // start of R and C, past the buffers' end for rows >= M.  The table
+  // entries come by vector loads at the start of the tile-boundary phase,
+  // before its copies, so that waiting for them never waits for the copies
+  // (scalar loads would each need 8 SGPRs and run one after another).
+  constexpr bool SCATTER = ROWS && RESID;
+  unsigned roff[SCATTER ? NOUT : 1];
+  auto load_rows = [&](int m0, int n0) __attribute__((always_inline)) {
+    if constexpr (SCATTER) {
+      int src[NOUT];
+#pragma unroll
+      for (int k = 0; k < NOUT; ++k) src[k] = rows_table[m0 + wm * 128 + 8 * k + (lane >> 3)];
+#pragma unroll
+      for (int k = 0; k < NOUT; ++k)
+        roff[k] = m0 + wm * 128 + 8 * k + (lane >> 3) < M
+                      ? (unsigned)(src[k] * Nc + n0 + wn * WN + (lane & 7) * 8) * 2u
+                      : 0xFFFFFFF0u;
+    }
+  };
   auto store_tile = [&](int m0, int n0) __attribute__((always_inline)) {
     m0 = __builtin_amdgcn_readfirstlane(m0);
     n0 = __builtin_amdgcn_readfirstlane(n0);
@@ -356,20 +376,6 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
     // soffset.  Each access covers 8 whole 128-byte rows.
     const unsigned st_base =
         (unsigned)((wm * 128 + (lane >> 3)) * Nc + wn * WN + (lane & 7) * 8) * 2u;
-    // With a row table (residual and output rows elsewhere): one offset per
-    // row from the start of R and C, past the buffers' end for rows >= M.
-    constexpr bool SCATTER = ROWS && RESID;
-    unsigned roff[SCATTER ? NOUT : 1];
-    if constexpr (SCATTER) {
-#pragma unroll
-      for (int k = 0; k < NOUT; ++k) {
-        const int rb = m0 + wm * 128 + 8 * k;  // uniform
-        const int src = pick8(*(const GS_CONST int8v*)(rows + rb), lane >> 3);
-        roff[k] = rb + (lane >> 3) < M
-                      ? (unsigned)(src * Nc + n0 + wn * WN + (lane & 7) * 8) * 2u
-                      : 0xFFFFFFF0u;
-      }
-    }
     // the output (and residual) through buffers over the tile's rows below
     // M, or over all M_cap rows of C (and R) with a row table
     auto rows_rsrc = [&](const bf16* base) __attribute__((always_inline)) {
@@ -519,6 +525,7 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
   auto run_stage = [&](bool first) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NSUB; ++u) {
+      if (SCATTER && u == 0 && first && have_prev) load_rows(m0p, n0p);
       if (u < NSUB - 1) {
         constexpr int NB = NSUB - 1;
         issue_copies(u * LPS / NB, (u + 1) * LPS / NB);
@@ -544,6 +551,7 @@ __global__ __launch_bounds__(pp::THREADS, 1) void gemm_pp_bf16_kernel(
     tile_of(++k, panel, col);
     if (panel < 0) break;
   }
+  load_rows(m0p, n0p);
   store_tile(m0p, n0p);
   if (grp == 0) barrier();  // as many barriers as group 1
   wait_vmem();
