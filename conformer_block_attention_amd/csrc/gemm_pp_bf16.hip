@@ -47,6 +47,12 @@
 //     their residual reads return zero.  (Letting such a row store a copy of
 //     row M-1 would race with C == R in place: another wave may already have
 //     written row M-1 when the copy reads its residual.)
+//   * row tables (the padded-bucket path, whose valid rows are scattered
+//     over the buckets): row r of the product is row rows[r] of A (without
+//     a residual: the copies read A's rows through the table) or of R and C
+//     (with one: the epilogue reads the residual and stores the output at
+//     per-row offsets, past the buffers' end for rows >= M).  A template
+//     parameter: without it the kernel is unchanged.
 //     Requires K % 64 == 0 and Nc % BN == 0.
 #include "attn_units.hpp"
 #include "gs_device.hpp"
