@@ -6,8 +6,8 @@ allocation (the workspace is the caller's, or the static per-GPU array of
 the no-allocation entry point).  Each replay runs after eager work on the
 same buffers (the output cleared by a fill kernel, the inputs read by other
 kernels) and must give the eager result bit for bit, for one layer, for a
-two-layer stack whose second layer reuses the first layer's unit table, and
-for the no-allocation entry point."""
+two-layer stack whose second layer reuses the first layer's unit table, for
+the no-allocation entry point and for the padded-bucket entry point."""
 import numpy as np
 import pytest
 import torch
@@ -69,3 +69,30 @@ def test_noalloc_entry_point_in_a_graph():
     with torch.cuda.graph(g):
         gsattn.block_mhsa_fwd_noalloc(x, cu, w1, o1, 200, 8, out=out)
     _replay_and_check(g, [out], [ref])
+
+
+def test_padded_entry_point_in_a_graph():
+    """The padded-bucket path (bucket offsets, row table with the unit table,
+    the two projections through the row table, the attention and the
+    padding-row copy) is kernels only as well: captured and replayed, it
+    gives the eager result bit for bit."""
+    d, H, B, T = 1024, 8, 200, 512
+    lengths = np.array([512, 0, 300, 77, 1, 511, 256, 200], dtype=np.int64)
+    S = len(lengths)
+    G.print_case("graph_padded", S=S, T=T)
+    case = workloads.custom_case(lengths, d, H, B, torch.bfloat16, seed=47)
+    wqkv, wo = (w.to(G.dev()) for w in case.weights[0])
+    g = torch.Generator(device=G.dev()).manual_seed(47)
+    x = torch.randn(S, T, d, generator=g, device=G.dev()).to(torch.bfloat16)
+    lens = torch.from_numpy(lengths.astype(np.int32)).to(G.dev())
+    ws = torch.empty(gsattn.load().gs_block_mhsa_padded_workspace_bytes(S, T, d, 1),
+                     dtype=torch.uint8, device=G.dev())
+    ref = gsattn.block_mhsa_fwd_padded(x, lens, wqkv, wo, B, H, workspace=ws).clone()
+    out = torch.empty_like(x)
+    gsattn.block_mhsa_fwd_padded(x, lens, wqkv, wo, B, H, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gsattn.block_mhsa_fwd_padded(x, lens, wqkv, wo, B, H, out=out, workspace=ws)
+    _replay_and_check(graph, [out], [ref])
