@@ -204,11 +204,28 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_bf16_nt_kernel(
   const int slot0 = by_xcd ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   const int per = by_xcd ? (Gs >> 3) : Gs;
   const int x_tiles = (p_hi - p_lo) * nt_count;
+  // One tile per workgroup (a round of small tiles): workgroup ids reach the
+  // XCDs round-robin, so the tiles of ids x, x + 8, ... share XCD x's L2.
+  // The order below gives each XCD whole groups of 8 panels (all column
+  // tiles of a few panels); when that makes an XCD read more rows of the
+  // operands than all panels of an eighth of the column tiles, the XCD takes
+  // the latter instead (the projection's 565 leftover rows: 9 panels of 64
+  // rows against 24 weight slices of 128).
+  const bool col_split = !by_xcd && (nt_count & 7) == 0 && (Gs & 7) == 0 &&
+                         (long long)mt_count * nt_count <= Gs &&
+                         mt_count * BM + (nt_count >> 3) * BN <
+                             ((mt_count + 7) >> 3) * BM + nt_count * BN;
   auto tile_of = [&](int k, int& panel, int& col) __attribute__((always_inline)) {
     const int u = slot0 + k * per;
     if (u >= x_tiles) {
       panel = -1;
       col = 0;
+      return;
+    }
+    if (col_split) {
+      const int slot = u >> 3;
+      col = (u & 7) * (nt_count >> 3) + slot / mt_count;
+      panel = slot - (slot / mt_count) * mt_count;
       return;
     }
     const int grp = u / (8 * nt_count);
