@@ -590,10 +590,14 @@ hipError_t launch_gemm_tail_bf16(const void* A, const void* W, const void* R, vo
 // after them run as a second launch of one round of small tiles (BM x 128,
 // BM chosen so that every tile has a CU of its own), if such a round can
 // hold them.  Returns the first row of that second part (M when one launch
-// is kept) and its row tile in *tail_bm.  For M = 55093 on 256 CUs: the
-// projection (12 tiles per panel) runs 213 panels in 10 rounds, then 565
-// rows as 216 tiles of 64 x 128; out_proj (4 tiles per panel) runs 192
-// panels in 3 rounds, then 6144 rows as 256 tiles of 192 x 128.
+// is kept, 0 when the small tiles take all rows) and its row tile in
+// *tail_bm.  For M = 55093 on 256 CUs: the projection (12 tiles per panel)
+// runs 213 panels in 10 rounds, then 565 rows as 216 tiles of 64 x 128;
+// out_proj (4 tiles per panel) runs 192 panels in 3 rounds, then 6144 rows
+// as 256 tiles of 192 x 128.  With fewer 256 x 256 tiles than CUs (a short
+// batch) the round of small tiles takes every row when it fits: for
+// M = 800 the projection runs 168 tiles of 128 x 128 instead of 48 large
+// ones, out_proj 104 tiles of 64 x 128 instead of 16.
 static int pp_split_rows(int M, int Nc, int* tail_bm) {
   const int tiles_per_panel = Nc / 256;
   const int mt = (M + pp::BM - 1) / pp::BM;
@@ -601,7 +605,13 @@ static int pp_split_rows(int M, int Nc, int* tail_bm) {
   const long long tiles = (long long)mt * tiles_per_panel;
   const long long rounds = tiles / cus;
   *tail_bm = 0;
-  if (rounds < 1 || tiles % cus == 0) return M;
+  if (rounds < 1) {
+    const int bm = gemm_tail_tile_rows(M, Nc);
+    if (bm == 0) return M;
+    *tail_bm = bm;
+    return 0;
+  }
+  if (tiles % cus == 0) return M;
   const int main_panels = (int)(rounds * cus / tiles_per_panel);
   const int rest = M - main_panels * pp::BM;
   if (rest <= 0) return M;
@@ -630,8 +640,11 @@ static hipError_t pp_launch(const bf16* A, const bf16* W, const bf16* R, bf16* C
   }
   int tail_bm = 0;
   const int m1 = pp_split_rows(M, Nc, &tail_bm);
-  launch(m1, nullptr);
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (m1 > 0) {
+    launch(m1, nullptr);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess || m1 == M) return e;
   const size_t a_off = (size_t)m1 * K, c_off = (size_t)m1 * Nc;
   e = launch_gemm_tail_bf16(A + a_off, W, RESID ? R + c_off : nullptr, C + c_off, M - m1, Nc, K,
