@@ -11,6 +11,7 @@
 namespace gs {
 
 constexpr int F32_BM = 64, F32_BN = 64, F32_BK = 16, F32_PAD = 4;
+constexpr int F32_PF = 4;  // K steps whose loads are in flight
 
 template <bool RESID>
 __global__ __launch_bounds__(256) void gemm_f32_nt_kernel(const float* __restrict__ A,
@@ -35,26 +36,48 @@ __global__ __launch_bounds__(256) void gemm_f32_nt_kernel(const float* __restric
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < K; k0 += F32_BK) {
-    const float4 a = *(const float4*)(A + (size_t)ar * K + k0 + lk);
-    const float4 w = *(const float4*)(W + (size_t)br * K + k0 + lk);
-    __syncthreads();
-    As[lk + 0][lr] = a.x; As[lk + 1][lr] = a.y; As[lk + 2][lr] = a.z; As[lk + 3][lr] = a.w;
-    Bs[lk + 0][lr] = w.x; Bs[lk + 1][lr] = w.y; Bs[lk + 2][lr] = w.z; Bs[lk + 3][lr] = w.w;
-    __syncthreads();
+  // The loads of a K step are issued F32_PF steps before the step stages
+  // them in LDS, so a workgroup alone on its CU (a short batch) does not
+  // wait for each step's loads in turn.
+  const float* ap = A + (size_t)ar * K + lk;
+  const float* wp = W + (size_t)br * K + lk;
+  const int ksteps = K / F32_BK;
+  float4 a[F32_PF], w[F32_PF];
 #pragma unroll
-    for (int ks = 0; ks < F32_BK / 4; ++ks) {
-      const int k = ks * 4 + (lane >> 4);
-      float af[2], bf[2];
+  for (int p = 0; p < F32_PF; ++p) {
+    if (p < ksteps) {
+      a[p] = *(const float4*)(ap + p * F32_BK);
+      w[p] = *(const float4*)(wp + p * F32_BK);
+    }
+  }
+  for (int s0 = 0; s0 < ksteps; s0 += F32_PF) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = As[k][wm * 32 + i * 16 + (lane & 15)];
+    for (int p = 0; p < F32_PF; ++p) {
+      const int s = s0 + p;
+      if (s >= ksteps) break;
+      const float4 ca = a[p], cw = w[p];
+      if (s + F32_PF < ksteps) {
+        a[p] = *(const float4*)(ap + (s + F32_PF) * F32_BK);
+        w[p] = *(const float4*)(wp + (s + F32_PF) * F32_BK);
+      }
+      __syncthreads();
+      As[lk + 0][lr] = ca.x; As[lk + 1][lr] = ca.y; As[lk + 2][lr] = ca.z; As[lk + 3][lr] = ca.w;
+      Bs[lk + 0][lr] = cw.x; Bs[lk + 1][lr] = cw.y; Bs[lk + 2][lr] = cw.z; Bs[lk + 3][lr] = cw.w;
+      __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = Bs[k][wn * 32 + j * 16 + (lane & 15)];
+      for (int ks = 0; ks < F32_BK / 4; ++ks) {
+        const int k = ks * 4 + (lane >> 4);
+        float af[2], bf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) af[i] = As[k][wm * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j], af[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) bf[j] = Bs[k][wn * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j], af[i], acc[i][j], 0, 0, 0);
+      }
     }
   }
 
