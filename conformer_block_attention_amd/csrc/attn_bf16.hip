@@ -907,15 +907,44 @@ __global__ __launch_bounds__(1024) void build_unit_table_kernel(UnitTableJob j) 
 
 static int g_num_cus = 0;
 
+static int attn_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_num_cus = n;
+  }
+  return g_num_cus;
+}
+
 int attn_bf16_table_entries(long long N) { return (int)(N + 1); }
+
+// Query rows per unit.  A unit normally takes ATT_QG = 224 rows, all 7 math
+// waves, two to a SIMD on three of the SIMDs.  When a batch is so short that
+// units of 96 rows still give every item a CU of its own (an 800-frame
+// sequence: 4 blocks x 8 heads = 32 items of 224 rows, or 96 items of 96,
+// 96 and 8 rows), its blocks are cut into 96-row units: three times the
+// items on otherwise idle CUs, each with the math waves of query slots 0-2,
+// which sit on SIMDs 0-2, one per SIMD, so that no two share a matrix pipe
+// (slot 3 would share SIMD 0).  Each 32-row group of queries still runs
+// whole on one wave (96 = 3 x 32), so the results are the same bits.  A
+// function of the host's sizes only: the table's builder and the attention
+// launch agree on it.
+static int attn_bf16_qg(long long N, int S, int B, int heads) {
+  constexpr int QG_SHORT = 3 * ATT_QW;
+  static_assert(QG_SHORT % ATT_QW == 0 && QG_SHORT < ATT_QG, "short-batch unit");
+  const long long items = (long long)attn_unit_bound(N, S, B, QG_SHORT) * heads;
+  return items <= attn_cus() ? QG_SHORT : ATT_QG;
+}
 
 // The unit-table build of a launch over these spans, for another launch to
 // run in a spare workgroup (the table in the workspace `table`, then,
 // 256-byte aligned, one overflow flag word per unit).
-UnitTableJob attn_bf16_table_job(SeqSpans sp, int S, long long N, int B, void* table) {
+UnitTableJob attn_bf16_table_job(SeqSpans sp, int S, long long N, int B, int heads, void* table) {
   unsigned long long* ovf =
       (unsigned long long*)((char*)table + ((16 * (N + 1) + 255) / 256) * 256);
-  return UnitTableJob{sp, S, B, ATT_QG, ATT_KC, (int4*)table, ovf};
+  return UnitTableJob{sp, S, B, attn_bf16_qg(N, S, B, heads), ATT_KC, (int4*)table, ovf};
 }
 
 // build_table = false: `table` already holds the unit table of these spans
@@ -924,23 +953,16 @@ UnitTableJob attn_bf16_table_job(SeqSpans sp, int S, long long N, int B, void* t
 hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long N, int d,
                                   int heads, int B, void* o, void* table, hipStream_t stream,
                                   bool build_table) {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    g_num_cus = n;
-  }
-  const UnitTableJob job = attn_bf16_table_job(sp, S, N, B, table);
+  const UnitTableJob job = attn_bf16_table_job(sp, S, N, B, heads, table);
   unsigned long long* ovf = job.flags;
   if (build_table) {
     hipLaunchKernelGGL(build_unit_table_kernel, dim3(1), dim3(1024), 0, stream, job);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const long long units = attn_unit_bound(N, S, B, ATT_QG);
+  const long long units = attn_unit_bound(N, S, B, job.qg);
   const long long items = units * heads;
-  const int grid = items < g_num_cus ? (int)items : g_num_cus;
+  const int grid = items < attn_cus() ? (int)items : attn_cus();
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
   hipLaunchKernelGGL(block_attn_bf16_kernel, dim3(grid), dim3(ATT_THREADS), 0, stream,
                      (const bf16*)qkv, (int4*)table, ovf, heads, d, scale_log2, (bf16*)o);

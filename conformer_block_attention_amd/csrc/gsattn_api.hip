@@ -19,7 +19,8 @@ namespace gs {
 hipError_t launch_qkv_proj_bf16(const void* x, const void* wqkv, void* qkv, int M, int d,
                                 hipStream_t stream, const UnitTableJob* job = nullptr,
                                 bool* job_done = nullptr);
-UnitTableJob attn_bf16_table_job(SeqSpans sp, int S, long long N, int B, void* table);
+UnitTableJob attn_bf16_table_job(SeqSpans sp, int S, long long N, int B, int heads,
+                                  void* table);
 hipError_t launch_out_proj_bf16(const void* o, const void* wo, const void* x, void* out, int M,
                                 int d, hipStream_t stream);
 hipError_t launch_block_attn_bf16(const void* qkv, SeqSpans sp, int S, long long N, int d,
@@ -528,7 +529,7 @@ gs_status gs_block_mhsa_fwd(const void* x, const int32_t* cu_seqlens, const void
     // attention's unit table in a workgroup of its own
     const gs::UnitTableJob job = gs::attn_bf16_table_job(gs::SeqSpans{cu_seqlens, 0},
                                                          desc->num_seqs, p.N, block_frames,
-                                                         p.table);
+                                                         heads, p.table);
     GS_TRY(hip_status(gs::launch_qkv_proj_bf16(x, Wqkv, p.qkv, (int)p.N, p.d, stream, &job,
                                                &table_built),
                       "qkv_proj launch"));
@@ -624,7 +625,7 @@ gs_status gs_block_mhsa_fwd_padded(const void* x, const int32_t* lengths, int32_
                        (const int*)lengths, S, (int)bucket_frames, cu);
     // (the attention's unit table is built in the same launch)
     const gs::UnitTableJob job = gs::attn_bf16_table_job(gs::SeqSpans{cu, 0}, S, p.N,
-                                                         block_frames, p.table);
+                                                         block_frames, heads, p.table);
     hipLaunchKernelGGL(gs::padded_rows_table_kernel, dim3((bucket_frames + 255) / 256, S + 1),
                        dim3(256), 0, stream, (const int*)lengths, (const int*)cu,
                        (int)bucket_frames, rows, job);
