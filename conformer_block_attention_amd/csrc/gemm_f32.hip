@@ -1,17 +1,17 @@
 // gemm_f32.hip -- IEEE fp32 GEMM for the projections (fp32 workloads):
 //   C[M][Nc] = (R[M][Nc] +) A[M][K] . W[Nc][K]^T
 // on v_mfma_f32_16x16x4_f32 (fp32 products and sums, no reduced-precision
-// inputs).  Macro tile 64 x 64, K step 16, 4 waves each 32 x 32 (2 x 2 MFMA
+// inputs).  Macro tile 64 x 64, K step 32, 4 waves each 32 x 32 (2 x 2 MFMA
 // tiles).  Tiles are staged k-major in LDS ([k][row], padded) so that one MFMA
 // operand read is 16 consecutive rows of one k.  The weight fragment is the
 // first MFMA operand, so each lane holds 4 consecutive output columns.
-// K must be a multiple of 16 and Nc a multiple of 4; M is arbitrary.
+// K must be a multiple of 32 and Nc a multiple of 4; M is arbitrary.
 #include "gs_device.hpp"
 
 namespace gs {
 
-constexpr int F32_BM = 64, F32_BN = 64, F32_BK = 16, F32_PAD = 4;
-constexpr int F32_PF = 4;  // K steps whose loads are in flight
+constexpr int F32_BM = 64, F32_BN = 64, F32_BK = 32, F32_PAD = 4;
+constexpr int F32_PF = 2;  // K steps whose loads are in flight
 
 template <bool RESID>
 __global__ __launch_bounds__(256) void gemm_f32_nt_kernel(const float* __restrict__ A,
@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void gemm_f32_nt_kernel(const float* __restric
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.x * F32_BM, n0 = blockIdx.y * F32_BN;
 
-  // loader: thread -> row tid/4, k (tid%4)*4 .. +3
+  // loader: thread -> row tid/4, k (tid%4)*4 .. +3 and 16 further on
   const int lr = tid >> 2, lk = (tid & 3) * 4;
   int ar = m0 + lr; ar = ar < M ? ar : M - 1;
   int br = n0 + lr; br = br < Nc ? br : Nc - 1;
@@ -42,27 +42,36 @@ __global__ __launch_bounds__(256) void gemm_f32_nt_kernel(const float* __restric
   const float* ap = A + (size_t)ar * K + lk;
   const float* wp = W + (size_t)br * K + lk;
   const int ksteps = K / F32_BK;
-  float4 a[F32_PF], w[F32_PF];
+  float4 a[F32_PF][2], w[F32_PF][2];
+  auto load = [&](int p, int s) __attribute__((always_inline)) {
 #pragma unroll
-  for (int p = 0; p < F32_PF; ++p) {
-    if (p < ksteps) {
-      a[p] = *(const float4*)(ap + p * F32_BK);
-      w[p] = *(const float4*)(wp + p * F32_BK);
+    for (int h = 0; h < 2; ++h) {
+      a[p][h] = *(const float4*)(ap + s * F32_BK + h * 16);
+      w[p][h] = *(const float4*)(wp + s * F32_BK + h * 16);
     }
-  }
+  };
+#pragma unroll
+  for (int p = 0; p < F32_PF; ++p)
+    if (p < ksteps) load(p, p);
   for (int s0 = 0; s0 < ksteps; s0 += F32_PF) {
 #pragma unroll
     for (int p = 0; p < F32_PF; ++p) {
       const int s = s0 + p;
       if (s >= ksteps) break;
-      const float4 ca = a[p], cw = w[p];
-      if (s + F32_PF < ksteps) {
-        a[p] = *(const float4*)(ap + (s + F32_PF) * F32_BK);
-        w[p] = *(const float4*)(wp + (s + F32_PF) * F32_BK);
+      float4 ca[2], cw[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        ca[h] = a[p][h];
+        cw[h] = w[p][h];
       }
+      if (s + F32_PF < ksteps) load(p, s + F32_PF);
       __syncthreads();
-      As[lk + 0][lr] = ca.x; As[lk + 1][lr] = ca.y; As[lk + 2][lr] = ca.z; As[lk + 3][lr] = ca.w;
-      Bs[lk + 0][lr] = cw.x; Bs[lk + 1][lr] = cw.y; Bs[lk + 2][lr] = cw.z; Bs[lk + 3][lr] = cw.w;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = lk + h * 16;
+        As[k + 0][lr] = ca[h].x; As[k + 1][lr] = ca[h].y; As[k + 2][lr] = ca[h].z; As[k + 3][lr] = ca[h].w;
+        Bs[k + 0][lr] = cw[h].x; Bs[k + 1][lr] = cw[h].y; Bs[k + 2][lr] = cw[h].z; Bs[k + 3][lr] = cw[h].w;
+      }
       __syncthreads();
 #pragma unroll
       for (int ks = 0; ks < F32_BK / 4; ++ks) {
