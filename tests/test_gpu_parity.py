@@ -660,8 +660,8 @@ def test_workload_chain16_teacher_forced(orc):
     and the softmax sharpens, so the rounding of Q and K to bf16 alone moves
     later layers' outputs by more than 2e-2 of their RMS.  Each layer is
     therefore checked teacher-forced on sampled blocks (first, last, two
-    tails, three random); every layer on every row in the test after this
-    one."""
+    tails, three random); every third layer (1, 4, ..., 16) on every row in
+    the test after this one."""
     G.print_case("bf16_b128_chain16")
     case = workloads.build_case(workloads.WORKLOADS["bf16_b128_chain16"])
     assert len(case.weights) == 16
@@ -674,7 +674,7 @@ def test_workload_chain16_teacher_forced(orc):
         cur = out
 
 
-@pytest.mark.parametrize("layer", list(range(16)))
+@pytest.mark.parametrize("layer", [0, 3, 6, 9, 12, 15])
 def test_workload_chain16_full_layer(orc, layer):
     """The chain run on the GPU up to `layer`, whose every row is then
     checked teacher-forced (as in the sampled test above)."""
