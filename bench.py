@@ -175,6 +175,59 @@ def time_steps(step, steps: int, stream):
     return np.array([bev.elapsed_ms(k, k + 1) for k in range(steps)]), el
 
 
+def _hwmon_power_file():
+    """The GPU's board-power reading in sysfs (microwatts), if there is one."""
+    import glob
+    for pat in ("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input",
+                "/sys/class/drm/card*/device/hwmon/hwmon*/power1_average"):
+        for f in sorted(glob.glob(pat)):
+            try:
+                with open(f) as fh:
+                    int(fh.read().strip())
+                return f
+            except (OSError, ValueError):
+                continue
+    return None
+
+
+def board_power(step, seconds: float = 3.0, settle: float = 1.0):
+    """Mean board power while step() runs back to back for `seconds`: the
+    hwmon reading sampled every 20 ms by a thread, after `settle` seconds in
+    which the board ramps up from idle.  None if no reading is available."""
+    import threading
+
+    f = _hwmon_power_file()
+    if f is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            if time.perf_counter() - t0 >= settle:
+                try:
+                    with open(f) as fh:
+                        samples.append(int(fh.read().strip()) / 1e6)
+                except (OSError, ValueError):
+                    pass
+            time.sleep(0.02)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"mean": float(np.mean(samples)), "max": float(np.max(samples)),
+            "samples": len(samples), "window_s": seconds - settle, "source": f}
+
+
 def bench_xattn(args):
     """The window cross-attention of the Q-Former projector on its workload."""
     w = workloads.XATTN_WORKLOADS[args.workload]
@@ -406,6 +459,8 @@ def main():
                     choices=workloads.WORKLOAD_ORDER + list(workloads.XATTN_WORKLOADS) +
                     [CTC_WORKLOAD])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the 3 s pass that reads the board power")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB MiB, 5 times")
@@ -497,6 +552,8 @@ def main():
         step(ev, 4 * nl * k)
     torch.cuda.synchronize()
 
+    power = None if args.no_power else board_power(step)
+
     per = {k: [] for k in KERNELS}
     for i in range(nl * args.steps):
         b = 4 * i
@@ -568,6 +625,10 @@ def main():
         "roofline": roof,
         "counters": (counters_for(dom, w.name, fl[dom] / (avg_ms[dom] * 1e-3) / 1e12)
                      if bf16 else None),
+        # board power while the step runs back to back (hwmon, after a 1 s
+        # ramp), and the energy of one step at that power
+        "board_power_w": (dict(power, joules_per_step=power["mean"] * ms_step * 1e-3)
+                          if power else None),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
